@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the mHC seam block on one MI355X.
+
+A step is one pass of the seam's hot path over one batch of T = 16384 tokens
+(n = 4 streams, hidden C = 5120, fused RMSNorm, 20 Sinkhorn iterations):
+    mhc_pre_delayed(x, pre_in) -> pre_out, post, comb, layer_input
+    mhc_post(y' = layer_input, x, post, comb) -> next residual
+(the sublayer between them is the identity stand-in; attention / MoE are not
+part of the seam).  Inputs are synthetic, seeded, and resident in HBM before
+the timed region.  Prints one JSON line.
+
+Also reported: per-kernel durations from HIP events on the launch stream, the
+roofline of the dominant kernel, a microseconds-per-call sweep at T = 1..128
+(graph replay and eager), the model-entry seam, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+T_SEAM = 16384
+C = 5120
+NS = 4
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "mHC seam tokens/s at T=16384 + µs/call T=1..128; HBM GB/s as % of peak"
+SWEEP_T = (1, 2, 4, 6, 7, 8, 16, 32, 64, 128)
+
+
+def pre_bytes(T, C=C, norm=True, delayed=True):
+    """Algorithmic HBM bytes of one pre call: x, layer_input, gates, pre_in, weights."""
+    K = NS * C
+    per_tok = K * 2 + C * 2 + (16 + 16 + 64) + (16 if delayed else 0)
+    fixed = K * 24 * 4 + 24 * 4 + 3 * 4 + (C * 2 if norm else 0)
+    return T * per_tok + fixed
+
+
+def post_bytes(T, C=C):
+    """Algorithmic HBM bytes of one post call: y, x, out, post, comb."""
+    return T * (C * 2 + 2 * NS * C * 2 + 16 + 64)
+
+
+def entry_bytes(T, C=C, norm=True):
+    return T * (C * 2 + NS * C * 2 + C * 2 + 96) + C * 24 * 4 + 108 + (C * 2 if norm else 0)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the T=1..128 sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU oracle sample time")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: measures one GPU only (--gpus 1). The seam is per-token, so more GPUs "
+              "would each run the same kernels on their own share of tokens with no exchange; "
+              "no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_mhc_pre_amd as M
+    import mhc_inputs as mi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    # ---------------------------------------------------------------- seam inputs (HBM-resident)
+    t0 = time.time()
+    d = mi.pre_inputs(T_SEAM, seed=2, delayed=True, norm=True, outlier_frac=0.01)
+    x = bf(d["x"])
+    pre_in = f32(d["pre_in"])
+    nw = bf(d["norm_weight"])
+    w = M.make_weights(f32(d["fn"]), f32(d["bias"]), f32(d["alpha"]))
+    x_host_sample = d["x"][:4096].copy()
+    pre_in_host_sample = d["pre_in"][:4096].copy()
+    fn_h, bias_h, alpha_h, nw_h = d["fn"], d["bias"], d["alpha"], d["norm_weight"]
+    del d
+    pre_out, post, comb, li = M._pre_outputs(T_SEAM, C, dev)
+    out = torch.empty_like(x)
+    ws = M.workspace(dev, T_SEAM, C)
+    torch.cuda.synchronize()
+    print("inputs ready in %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.mhc_pre_delayed(x, pre_in, w, nw, 1e-6, 20, out=(pre_out, post, comb, li), ws=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        M.mhc_post(li, x, post, comb, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    post_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = t_total * 1e3 / args.steps
+    value = T_SEAM * args.steps / t_total
+
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    post_avg = sum(post_ms) / len(post_ms)
+    pb, qb = pre_bytes(T_SEAM), post_bytes(T_SEAM)
+    kernels = {
+        "mhc_pre_kernel<delayed>": dict(avg_us=pre_avg * 1e3, alg_bytes=pb,
+                                        gbs=pb / (pre_avg * 1e-3) / 1e9),
+        "mhc_post_kernel": dict(avg_us=post_avg * 1e3, alg_bytes=qb, gbs=qb / (post_avg * 1e-3) / 1e9),
+    }
+    for v in kernels.values():
+        v["frac"] = v["gbs"] / HBM_PEAK_GBS
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    traffic = None
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(kernels[dom]["gbs"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kernels[dom]["frac"], 4),
+                "traffic": traffic}
+    seam_gbs = (pb + qb) / (t_total / args.steps) / 1e9
+
+    # ---------------------------------------------------------------- T = 1..128 sweep
+    sweep = None
+    if not args.no_sweep:
+        sweep = run_sweep(torch, M, mi, dev, bf, f32, w, nw)
+    entry = None if args.no_sweep else run_entry(torch, M, mi, dev, bf, f32)
+
+    del x, out, li
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(x_host_sample, pre_in_host_sample, fn_h, bias_h, alpha_h, nw_h,
+                           args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "mhc seam: pre_delayed + fused RMSNorm + post, T=16384, n=4, C=5120, "
+                               "20 Sinkhorn iters, 1% outlier rows x100",
+                   "T": T_SEAM, "hc_mult": NS, "hidden": C, "sinkhorn_iters": 20,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "seam_alg_GBps": round(seam_gbs, 1),
+        "launches_per_seam": 2,
+        "us_per_call_sweep": sweep,
+        "entry": entry,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _median_us(fn, torch, reps=5, iters=200):
+    """Median over `reps` of the mean time of `iters` back-to-back calls (HIP events)."""
+    out = []
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn(iters)
+        e.record()
+        e.synchronize()
+        out.append(s.elapsed_time(e) * 1e3 / iters)
+    return statistics.median(out)
+
+
+def run_sweep(torch, M, mi, dev, bf, f32, w, nw):
+    res = {}
+    for T in SWEEP_T:
+        d = mi.pre_inputs(T, seed=50 + T, delayed=True)
+        x = bf(d["x"])
+        pin = f32(d["pre_in"])
+        outs = M._pre_outputs(T, C, dev)
+        xo = torch.empty_like(x)
+        ws = M.workspace(dev, T, C)
+
+        def pre_call():
+            M.mhc_pre_delayed(x, pin, w, nw, 1e-6, 20, out=outs, ws=ws)
+
+        def post_call():
+            M.mhc_post(outs[3], x, outs[1], outs[2], out=xo)
+
+        def seam_call():
+            pre_call()
+            post_call()
+
+        row = {}
+        for name, fn in (("pre_delayed", pre_call), ("post", post_call), ("seam", seam_call)):
+            fn()
+            torch.cuda.synchronize()
+            # eager: host launch path included
+            row[name + "_eager_us"] = round(_median_us(lambda n: [fn() for _ in range(n)], torch), 2)
+            # graph replay: 20 calls captured once, replayed 10x per sample
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    for _ in range(20):
+                        fn()
+            torch.cuda.current_stream().wait_stream(s)
+            g.replay()
+            torch.cuda.synchronize()
+            row[name + "_graph_us"] = round(_median_us(lambda n: [g.replay() for _ in range(n // 20)],
+                                                       torch), 2)
+            del g
+        res[str(T)] = row
+    return res
+
+
+def run_entry(torch, M, mi, dev, bf, f32):
+    res = {}
+    for T in (1, 128, T_SEAM):
+        d = mi.entry_inputs(T, seed=999)
+        h = bf(d["h"])
+        we = M.make_weights(f32(d["fn"]), f32(d["bias"]), f32(d["alpha"]))
+        nw = bf(d["norm_weight"])
+        ws = M.workspace(dev, T, C)
+        o = M.mhc_broadcast_entry(h, we, nw, 1e-6, 20, ws=ws)
+        torch.cuda.synchronize()
+        us = _median_us(lambda n: [M.mhc_broadcast_entry(h, we, nw, 1e-6, 20, out=o, ws=ws)
+                                   for _ in range(n)], torch, reps=3, iters=20 if T > 1024 else 100)
+        res[str(T)] = {"us": round(us, 2), "alg_GBps": round(entry_bytes(T) / (us * 1e-6) / 1e9, 1)}
+        del o, h
+    return res
+
+
+def cpu_baseline(x, pre_in, fn, bias, alpha, nw, target_s):
+    """The oracle as it stands (float64 C, OpenMP over tokens) on a bounded
+    sample of the same seam: pre_delayed with fused norm, then post."""
+    import oracle
+    oracle.lib()
+    threads = oracle.max_threads()
+
+    def run(S):
+        t = time.perf_counter()
+        o = oracle.mhc_pre_delayed(x[:S], pre_in[:S], fn, bias, alpha, 1e-6, 20, norm_weight=nw)
+        post = o["post"].astype(np.float32)
+        comb = o["comb"].astype(np.float32)
+        oracle.mhc_post(o["li"], x[:S], post, comb)
+        return time.perf_counter() - t
+
+    S = min(len(x), 2048)
+    run(64)  # warm-up (page in, thread pool)
+    reps, dt = 0, 0.0
+    while dt < target_s and reps < 1000:
+        dt += run(S)
+        reps += 1
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(S * reps / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d tokens of the T=16384 seam input (pre_delayed+norm then post) x %d passes, "
+                      "%.1f s; %s" % (S, reps, dt, cpu_model)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+"""decode_mhc_pre_amd -- the mHC seam block on MI355X (gfx950).
+
+A thin ctypes binding over ``libmhc.so`` (C ABI in ``include/mhc.h``).  It only
+marshals arguments: tensors become device pointers, the current HIP stream is
+passed along, outputs are allocated with torch.  Every step of the seam runs in
+the library's HIP kernels; there is no fallback path.  If the library is not
+built, importing the ops raises.
+
+Entry points (same names as the C ABI):
+    mhc_pack_fn, mhc_pre, mhc_pre_delayed, mhc_post, mhc_broadcast_entry,
+    mhc_workspace_bytes, mhc_fn_packed_bytes, mhc_status_str
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+from . import build as _build
+
+HC_MULT = 4
+NUM_LOGITS = 24
+
+STATUS = {
+    0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_UNSUPPORTED",
+    4: "MHC_ERR_ALIGN", 5: "MHC_ERR_ALIAS", 6: "MHC_ERR_WORKSPACE", 7: "MHC_ERR_HIP",
+}
+
+
+class MhcError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s" % (what, mhc_status_str(status)))
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("fn_packed", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("alpha", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmhc.so (built in-tree by __graft_entry__.build() / build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise ImportError("libmhc.so is not built (%s); run `python -m decode_mhc_pre_amd.build`"
+                              % _build.LIB)
+        L = ctypes.CDLL(_build.LIB)
+        P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.mhc_fn_packed_bytes.argtypes = [I]
+        L.mhc_fn_packed_bytes.restype = Z
+        L.mhc_pack_fn.argtypes = [P, I, P, P]
+        L.mhc_workspace_bytes.argtypes = [I, I, I]
+        L.mhc_workspace_bytes.restype = Z
+        L.mhc_pre.argtypes = [P, I, I, I, _Weights, P, F, I, P, P, P, P, P, Z, P]
+        L.mhc_pre_delayed.argtypes = [P, P, I, I, I, _Weights, P, F, I, P, P, P, P, P, Z, P]
+        L.mhc_post.argtypes = [P, P, P, P, I, I, I, P, P]
+        L.mhc_broadcast_entry.argtypes = [P, I, I, I, _Weights, P, F, I, P, P, P, P, P, P, Z, P]
+        for f in ("mhc_pack_fn", "mhc_pre", "mhc_pre_delayed", "mhc_post", "mhc_broadcast_entry"):
+            getattr(L, f).restype = I
+        L.mhc_status_str.argtypes = [I]
+        L.mhc_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+EXPORTS = ("mhc_fn_packed_bytes", "mhc_pack_fn", "mhc_workspace_bytes", "mhc_pre",
+           "mhc_pre_delayed", "mhc_post", "mhc_broadcast_entry", "mhc_status_str")
+
+
+def mhc_status_str(status: int) -> str:
+    return lib().mhc_status_str(int(status)).decode()
+
+
+def mhc_fn_packed_bytes(K: int) -> int:
+    return int(lib().mhc_fn_packed_bytes(int(K)))
+
+
+def mhc_workspace_bytes(T_max: int, n: int = HC_MULT, C: int = 5120) -> int:
+    return int(lib().mhc_workspace_bytes(int(T_max), int(n), int(C)))
+
+
+# ----------------------------------------------------------------------------- torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MhcError(status, what)
+
+
+def _u16(t):
+    """bf16 tensor -> same storage viewed as int16 (the ABI takes bit patterns)."""
+    torch = _torch()
+    if t is None:
+        return None
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError("expected a bfloat16 tensor, got %s" % t.dtype)
+
+
+@dataclass
+class Weights:
+    """Weights of one seam on the device: fn packed for the library, bias [24], alpha [3]."""
+    fn_packed: object
+    bias: object
+    alpha: object
+    K: int
+
+    def as_c(self) -> _Weights:
+        return _Weights(self.fn_packed.data_ptr(), self.bias.data_ptr(), self.alpha.data_ptr())
+
+
+def mhc_pack_fn(fn, out=None):
+    """Pack fn [K, 24] float32 (device) for the library; returns a uint8 device tensor."""
+    torch = _torch()
+    assert fn.dtype == torch.float32 and fn.dim() == 2 and fn.shape[1] == NUM_LOGITS and fn.is_contiguous()
+    K = fn.shape[0]
+    if out is None:
+        out = torch.empty(mhc_fn_packed_bytes(K), dtype=torch.uint8, device=fn.device)
+    _check(lib().mhc_pack_fn(_ptr(fn), K, _ptr(out), _stream(fn.device)), "mhc_pack_fn")
+    return out
+
+
+def make_weights(fn, bias, alpha) -> Weights:
+    """Device float32 fn [K,24], bias [24], alpha [3] -> packed Weights (packing runs once)."""
+    return Weights(mhc_pack_fn(fn), bias.contiguous(), alpha.contiguous(), int(fn.shape[0]))
+
+
+_ws_cache = {}
+
+
+def workspace(device, T: int, C: int):
+    """A zero-filled workspace large enough for T tokens (cached per device; one stream at a time)."""
+    torch = _torch()
+    need = max(mhc_workspace_bytes(max(T, 1), HC_MULT, C), 256)
+    key = (str(device), C)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _pre_outputs(T, C, dev, li=True):
+    torch = _torch()
+    pre = torch.empty((T, HC_MULT), dtype=torch.float32, device=dev)
+    post = torch.empty((T, HC_MULT), dtype=torch.float32, device=dev)
+    comb = torch.empty((T, HC_MULT, HC_MULT), dtype=torch.float32, device=dev)
+    lo = torch.empty((T, C), dtype=torch.bfloat16, device=dev) if li else None
+    return pre, post, comb, lo
+
+
+def mhc_pre(x, w: Weights, norm_weight=None, eps=1e-6, iters=20, out=None, ws=None):
+    """x [T,4,C] bf16 -> (pre [T,4], post [T,4], comb [T,4,4], layer_input [T,C] bf16)."""
+    T, n, C = x.shape
+    pre, post, comb, li = out if out is not None else _pre_outputs(T, C, x.device)
+    ws = workspace(x.device, T, C) if ws is None else ws
+    st = lib().mhc_pre(_ptr(_u16(x)), T, n, C, w.as_c(), _ptr(_u16(norm_weight)), float(eps), int(iters),
+                       _ptr(pre), _ptr(post), _ptr(comb), _ptr(li), _ptr(ws), ws.numel(),
+                       _stream(x.device))
+    _check(st, "mhc_pre")
+    return pre, post, comb, li
+
+
+def mhc_pre_delayed(x, pre_in, w: Weights, norm_weight=None, eps=1e-6, iters=20, out=None, ws=None):
+    """Delayed pre: collapse with pre_in [T,4] float32; returns (pre_out, post, comb, layer_input)."""
+    T, n, C = x.shape
+    pre, post, comb, li = out if out is not None else _pre_outputs(T, C, x.device)
+    ws = workspace(x.device, T, C) if ws is None else ws
+    st = lib().mhc_pre_delayed(_ptr(_u16(x)), _ptr(pre_in), T, n, C, w.as_c(), _ptr(_u16(norm_weight)),
+                               float(eps), int(iters), _ptr(pre), _ptr(post), _ptr(comb), _ptr(li),
+                               _ptr(ws), ws.numel(), _stream(x.device))
+    _check(st, "mhc_pre_delayed")
+    return pre, post, comb, li
+
+
+def mhc_post(y, x, post, comb, out=None):
+    """out [T,4,C] bf16 = post_i * y + sum_j comb_ij x_j; out may be x itself."""
+    torch = _torch()
+    T, n, C = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib().mhc_post(_ptr(_u16(y)), _ptr(_u16(x)), _ptr(post), _ptr(comb), T, n, C, _ptr(_u16(out)),
+                        _stream(x.device))
+    _check(st, "mhc_post")
+    return out
+
+
+def mhc_broadcast_entry(h, w: Weights, norm_weight=None, eps=1e-6, iters=20, layer_input=True,
+                        out=None, ws=None):
+    """h [T,C] bf16 -> (x_out [T,4,C], pre, post, comb, layer_input or None)."""
+    torch = _torch()
+    T, C = h.shape
+    if out is None:
+        x_out = torch.empty((T, HC_MULT, C), dtype=torch.bfloat16, device=h.device)
+        pre, post, comb, li = _pre_outputs(T, C, h.device, li=layer_input)
+    else:
+        x_out, pre, post, comb, li = out
+    ws = workspace(h.device, T, C) if ws is None else ws
+    st = lib().mhc_broadcast_entry(_ptr(_u16(h)), T, HC_MULT, C, w.as_c(), _ptr(_u16(norm_weight)),
+                                   float(eps), int(iters), _ptr(x_out), _ptr(pre), _ptr(post), _ptr(comb),
+                                   _ptr(li), _ptr(ws), ws.numel(), _stream(h.device))
+    _check(st, "mhc_broadcast_entry")
+    return x_out, pre, post, comb, li

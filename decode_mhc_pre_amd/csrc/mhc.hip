@@ -1,0 +1,274 @@
+// mhc.hip -- host side of libmhc: argument validation, launch planning and
+// the C ABI declared in include/mhc.h.  Everything is checked before anything
+// is enqueued; every launch goes to the caller's stream; nothing allocates.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "mhc.h"
+#include "mhc_kernels.hpp"
+
+namespace {
+
+using namespace mhc;
+
+// Projection workgroups aimed for when few tokens: splitting the 4C row over
+// workgroups spreads the (L2/HBM-resident) projection weight over the chip.
+constexpr int kTargetProjGroups = 256;
+constexpr int kMinKBPerSplit = 4;  // one 32-k step per wave at least
+constexpr int kMaxC = 16384;
+
+struct Plan {
+  int ntile, nsplit, nproj;
+};
+
+Plan make_plan(int T, int KB) {
+  Plan pl;
+  pl.ntile = (T + kTileT - 1) / kTileT;
+  int ns = pl.ntile >= kTargetProjGroups ? 1 : (kTargetProjGroups + pl.ntile - 1) / pl.ntile;
+  int maxs = KB / kMinKBPerSplit;
+  if (maxs < 1) maxs = 1;
+  if (ns > maxs) ns = maxs;
+  pl.nsplit = ns;
+  pl.nproj = pl.ntile * ns;
+  return pl;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout for a plan: [counters: ntile u32, padded to 256 B][partials].
+size_t counter_bytes(int ntile) { return align_up((size_t)ntile * sizeof(unsigned), 256); }
+size_t plan_ws_bytes(const Plan& pl) {
+  if (pl.nsplit <= 1) return 0;
+  return counter_bytes(pl.ntile) +
+         (size_t)pl.ntile * pl.nsplit * kTileT * kPartStride * sizeof(float);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Outputs must not overlap each other or any input.
+bool any_alias(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+  }
+  return false;
+}
+
+mhc_status check_common(int T, int n, int C) {
+  if (n != MHC_HC_MULT) return MHC_ERR_UNSUPPORTED;
+  if (C < 256 || C > kMaxC || C % 256 != 0) return MHC_ERR_UNSUPPORTED;
+  if (T < 0 || T > MHC_MAX_TOKENS) return MHC_ERR_SHAPE;
+  return MHC_OK;
+}
+
+mhc_status check_scalars(float eps, int iters) {
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return MHC_ERR_SHAPE;
+  if (iters < 1) return MHC_ERR_SHAPE;
+  return MHC_OK;
+}
+
+mhc_status launched() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MHC_OK : MHC_ERR_HIP;
+}
+
+// Shared by the three pre-stage entry points.
+mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, int n, int C,
+                      mhc_weights w, const uint16_t* norm_weight, float eps, int iters,
+                      uint16_t* x_out, float* pre, float* post, float* comb, uint16_t* li,
+                      void* ws, size_t ws_bytes, void* stream) {
+  mhc_status st = check_common(T, n, C);
+  if (st != MHC_OK) return st;
+  if ((st = check_scalars(eps, iters)) != MHC_OK) return st;
+  const bool entry = mode == kModeEntry;
+  if (!x || !w.fn_packed || !w.bias || !w.alpha || !pre || !post || !comb) return MHC_ERR_NULL;
+  if (mode == kModeDelayed && !pre_in) return MHC_ERR_NULL;
+  if (entry && !x_out) return MHC_ERR_NULL;
+  if (!entry && !li) return MHC_ERR_NULL;
+  const void* ptrs[] = {x, pre_in, w.fn_packed, w.bias, w.alpha, norm_weight, x_out,
+                        pre, post, comb, li, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MHC_ERR_ALIGN;
+
+  const int K = entry ? C : n * C;
+  const int KB = K / kKB;
+  const size_t Tz = (size_t)T;
+  const Range ins[] = {{x, Tz * K * 2},
+                       {pre_in, mode == kModeDelayed ? Tz * 16 : 0},
+                       {w.fn_packed, mhc_fn_packed_bytes(K)},
+                       {w.bias, 96},
+                       {w.alpha, 12},
+                       {norm_weight, norm_weight ? (size_t)C * 2 : 0}};
+  const Range outs[] = {{pre, Tz * 16},
+                        {post, Tz * 16},
+                        {comb, Tz * 64},
+                        {li, li ? Tz * C * 2 : 0},
+                        {x_out, entry ? Tz * n * C * 2 : 0},
+                        {ws, ws ? ws_bytes : 0}};
+  if (any_alias(outs, 6, ins, 6)) return MHC_ERR_ALIAS;
+
+  if (T == 0) return MHC_OK;
+  const Plan pl = make_plan(T, KB);
+  const size_t need = plan_ws_bytes(pl);
+  if (need > 0 && (!ws || ws_bytes < need)) return MHC_ERR_WORKSPACE;
+
+  PreParams p;
+  p.x = x;
+  p.pre_in = pre_in;
+  p.fnp = static_cast<const uint4*>(w.fn_packed);
+  p.bias = w.bias;
+  p.alpha = w.alpha;
+  p.nw = norm_weight;
+  p.pre = pre;
+  p.post = post;
+  p.comb = comb;
+  p.li = li;
+  p.xout = x_out;
+  p.cnt = need ? static_cast<unsigned*>(ws) : nullptr;
+  p.part = need ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(pl.ntile)) : nullptr;
+  p.eps = eps;
+  p.iters = iters;
+  p.T = T;
+  p.C = C;
+  p.K = K;
+  p.KB = KB;
+  p.ntile = pl.ntile;
+  p.nsplit = pl.nsplit;
+  p.nproj = pl.nproj;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 block(kThreads);
+  switch (mode) {
+    case kModePre:
+      hipLaunchKernelGGL(mhc_pre_kernel<kModePre>, dim3(pl.nproj), block, 0, s, p);
+      break;
+    case kModeDelayed:
+      hipLaunchKernelGGL(mhc_pre_kernel<kModeDelayed>, dim3(pl.nproj + T), block, 0, s, p);
+      break;
+    default:
+      hipLaunchKernelGGL(mhc_pre_kernel<kModeEntry>, dim3(pl.nproj), block, 0, s, p);
+      break;
+  }
+  return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mhc_fn_packed_bytes(int K) {
+  if (K <= 0) return 0;
+  return (size_t)K * kNL * 4;  // two bf16 per weight
+}
+
+mhc_status mhc_pack_fn(const float* fn, int K, void* fn_packed, void* stream) {
+  if (!fn || !fn_packed) return MHC_ERR_NULL;
+  if (K <= 0 || K % kKB != 0 || K > MHC_HC_MULT * kMaxC) return MHC_ERR_SHAPE;
+  if (!aligned16(fn) || !aligned16(fn_packed)) return MHC_ERR_ALIGN;
+  if (overlap({fn, (size_t)K * kNL * 4}, {fn_packed, mhc_fn_packed_bytes(K)})) return MHC_ERR_ALIAS;
+  const int KB = K / kKB;
+  const int total = KB * kFragPerKB * kWave;
+  hipLaunchKernelGGL(mhc_pack_fn_kernel, dim3((total + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), fn, KB, static_cast<uint4*>(fn_packed));
+  return launched();
+}
+
+size_t mhc_workspace_bytes(int T_max, int n, int C) {
+  if (n != MHC_HC_MULT || C < 256 || C > kMaxC || C % 256 != 0 || T_max <= 0) return 0;
+  size_t best = 0;
+  // the entry seam (K = C) and the 4-stream seams (K = 4C) may plan differently
+  const int KBs[2] = {C / kKB, MHC_HC_MULT * C / kKB};
+  const int ntile_max = (T_max + kTileT - 1) / kTileT;
+  for (int KB : KBs) {
+    for (int nt = 1; nt <= ntile_max && nt <= kTargetProjGroups; ++nt) {
+      const Plan pl = make_plan(nt * kTileT, KB);
+      const size_t b = plan_ws_bytes(pl);
+      if (b > best) best = b;
+    }
+  }
+  return best;
+}
+
+mhc_status mhc_pre(const uint16_t* x, int T, int n, int C, mhc_weights w,
+                   const uint16_t* norm_weight, float eps, int sinkhorn_iters, float* pre,
+                   float* post, float* comb, uint16_t* layer_input, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return pre_common(kModePre, x, nullptr, T, n, C, w, norm_weight, eps, sinkhorn_iters, nullptr,
+                    pre, post, comb, layer_input, workspace, workspace_bytes, stream);
+}
+
+mhc_status mhc_pre_delayed(const uint16_t* x, const float* pre_in, int T, int n, int C,
+                           mhc_weights w, const uint16_t* norm_weight, float eps,
+                           int sinkhorn_iters, float* pre_out, float* post, float* comb,
+                           uint16_t* layer_input, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return pre_common(kModeDelayed, x, pre_in, T, n, C, w, norm_weight, eps, sinkhorn_iters,
+                    nullptr, pre_out, post, comb, layer_input, workspace, workspace_bytes, stream);
+}
+
+mhc_status mhc_broadcast_entry(const uint16_t* h, int T, int n, int C, mhc_weights w_entry,
+                               const uint16_t* norm_weight, float eps, int sinkhorn_iters,
+                               uint16_t* x_out, float* pre, float* post, float* comb,
+                               uint16_t* layer_input, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return pre_common(kModeEntry, h, nullptr, T, n, C, w_entry, norm_weight, eps, sinkhorn_iters,
+                    x_out, pre, post, comb, layer_input, workspace, workspace_bytes, stream);
+}
+
+mhc_status mhc_post(const uint16_t* y, const uint16_t* x, const float* post, const float* comb,
+                    int T, int n, int C, uint16_t* out, void* stream) {
+  mhc_status st = check_common(T, n, C);
+  if (st != MHC_OK) return st;
+  if (!y || !x || !post || !comb || !out) return MHC_ERR_NULL;
+  const void* ptrs[] = {y, x, post, comb, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MHC_ERR_ALIGN;
+  const size_t Tz = (size_t)T;
+  const size_t xbytes = Tz * n * C * 2;
+  const Range o = {out, xbytes};
+  const Range ins_wo_x[] = {{y, Tz * C * 2}, {post, Tz * 16}, {comb, Tz * 64}};
+  for (const Range& r : ins_wo_x)
+    if (overlap(o, r)) return MHC_ERR_ALIAS;
+  if (static_cast<const void*>(out) != static_cast<const void*>(x) && overlap(o, {x, xbytes}))
+    return MHC_ERR_ALIAS;
+  if (T == 0) return MHC_OK;
+  const int C8 = C / 8;
+  const long long total = (long long)T * C8;
+  const unsigned grid = (unsigned)((total + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(mhc_post_kernel, dim3(grid), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), reinterpret_cast<const uint4*>(y),
+                     reinterpret_cast<const uint4*>(x), post, comb, reinterpret_cast<uint4*>(out),
+                     T, C8);
+  return launched();
+}
+
+const char* mhc_status_str(mhc_status s) {
+  switch (s) {
+    case MHC_OK: return "MHC_OK";
+    case MHC_ERR_NULL: return "MHC_ERR_NULL: a required pointer is NULL";
+    case MHC_ERR_SHAPE: return "MHC_ERR_SHAPE: bad token count, eps or iteration count";
+    case MHC_ERR_UNSUPPORTED: return "MHC_ERR_UNSUPPORTED: n must be 4 and C a multiple of 256 in [256, 16384]";
+    case MHC_ERR_ALIGN: return "MHC_ERR_ALIGN: pointers must be 16-byte aligned";
+    case MHC_ERR_ALIAS: return "MHC_ERR_ALIAS: an output overlaps an input or another output";
+    case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace missing or too small";
+    case MHC_ERR_HIP: return "MHC_ERR_HIP: the HIP runtime rejected the launch";
+  }
+  return "unknown mhc_status";
+}
+
+}  // extern "C"

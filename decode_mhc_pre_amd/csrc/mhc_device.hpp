@@ -1,0 +1,113 @@
+// mhc_device.hpp -- device building blocks of libmhc for gfx950 (CDNA4, wave64).
+//
+// The seam's hot path (vLLM PR "[ROCm][DSV4.1][Perf] Use AITER mHC for the
+// delayed pre block", Approach): projection of the flattened 4C row against fn
+// plus the row sum of squares, the gates and every Sinkhorn iteration, the
+// collapse of the four streams, and the folded RMSNorm of the "Fix TileLang
+// mHC pre on 64-wide wavefronts" PR (Measurements).  Every cross-lane
+// reduction here spans the full 64-lane wavefront and every role split is
+// wave-aligned: that PR's bug was a 32-lane role split inside a 64-lane wave
+// that summed only half of the squares (The bug).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mhc {
+
+constexpr int kNS = 4;        // residual streams (hc_mult)
+constexpr int kNL = 24;       // logits per token: pre 4 | post 4 | comb 16
+constexpr int kTileT = 16;    // tokens per projection tile = rows of one MFMA
+constexpr int kThreads = 256; // four waves per workgroup
+constexpr int kWave = 64;
+constexpr int kKB = 32;       // k elements per MFMA step (16x16x32)
+constexpr int kFragPerKB = 3; // 48 packed columns (24 hi | 24 lo) = 3 tiles of 16
+constexpr int kPartStride = 25; // 24 partial projections + partial sum of squares
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf_even(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_odd(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two floats -> two bf16 (round to nearest even), packed little-endian.
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  f[0] = bf_even(v.x); f[1] = bf_odd(v.x);
+  f[2] = bf_even(v.y); f[3] = bf_odd(v.y);
+  f[4] = bf_even(v.z); f[5] = bf_odd(v.z);
+  f[6] = bf_even(v.w); f[7] = bf_odd(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+}
+
+__device__ __forceinline__ float sumsq8(const uint4& v) {
+  float f[8];
+  unpack8(v, f);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = __builtin_fmaf(f[e], f[e], s);
+  return s;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const uint4& a, const uint4& b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- collapse
+// y_c = fl(fl(fl(fl(p0 x0) + fl(p1 x1)) + fl(p2 x2)) + fl(p3 x3)): each product
+// rounded to float, summed left to right over the streams, never fused --
+// the single-precision multiply-and-sum that the delayed-pre PR (Result)
+// reports as bit-exact between its paths.
+__device__ __forceinline__ float collapse1(float p0, float p1, float p2, float p3, float x0,
+                                           float x1, float x2, float x3) {
+#pragma clang fp contract(off)
+  float a = p0 * x0;
+  float b = p1 * x1;
+  float c = p2 * x2;
+  float d = p3 * x3;
+  return ((a + b) + c) + d;
+}
+
+__device__ __forceinline__ void collapse8(const uint4& v0, const uint4& v1, const uint4& v2,
+                                          const uint4& v3, float p0, float p1, float p2, float p3,
+                                          float (&y)[8]) {
+  float a[8], b[8], c[8], d[8];
+  unpack8(v0, a);
+  unpack8(v1, b);
+  unpack8(v2, c);
+  unpack8(v3, d);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = collapse1(p0, p1, p2, p3, a[e], b[e], c[e], d[e]);
+}
+
+// ---------------------------------------------------------------- reductions
+// Butterfly over all 64 lanes: every lane ends with the same bits (float
+// addition is commutative, so partner lanes form identical sums).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Sum over the 256-thread workgroup in a fixed order; every thread gets it.
+__device__ __forceinline__ float block_sum(float v, float* s_tmp) {
+  v = wave_sum(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) s_tmp[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float t = (s_tmp[0] + s_tmp[1]) + (s_tmp[2] + s_tmp[3]);
+  __syncthreads();
+  return t;
+}
+
+}  // namespace mhc

@@ -1,0 +1,156 @@
+/*
+ * mhc.h -- C ABI of libmhc, the mHC seam block (manifold-constrained
+ * hyper-connections) for AMD Instinct MI355X (gfx950).
+ *
+ * The seam sits between sublayers of a DeepSeek-V4.1-style decoder.  The
+ * residual carries n = 4 streams, x[T][4][C] in bf16.  The pre stage projects
+ * the RMS-scaled, flattened 4C row onto 24 logits ("mixes"), turns them into a
+ * sigmoid pre-mix, a post gate in (0,2) and a 4x4 comb matrix normalised by
+ * Sinkhorn iterations, and collapses the streams into the sublayer input
+ * (optionally through a folded RMSNorm).  The post stage writes the next
+ * residual, post_i * y + sum_j comb[i][j] x_j.
+ *
+ * Sources, cited by page title and section:
+ *   [p1] vLLM PR "[ROCm][DSV4.1][Perf] Use AITER mHC for the delayed pre block"
+ *   [p3] vLLM PR "[ROCm][DSv4.1] Fix TileLang mHC pre on 64-wide wavefronts and
+ *        use the fused kernels on the AMD path"
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is caller-owned DEVICE memory unless stated, and
+ *     must be 16-byte aligned.  bf16 tensors are passed as uint16_t bit
+ *     patterns; float tensors are IEEE single.  All arrays are dense row-major.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     null stream).  No call allocates memory, synchronises the host, or
+ *     compiles code, so calls may be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued and the status says why.  T == 0 is a no-op.
+ *   - Supported shapes: n == 4 (MHC_ERR_UNSUPPORTED otherwise); C a multiple
+ *     of 256 with 256 <= C <= 16384 (MHC_ERR_UNSUPPORTED otherwise);
+ *     0 <= T <= MHC_MAX_TOKENS (MHC_ERR_SHAPE otherwise).
+ *   - Outputs never overlap inputs or each other (MHC_ERR_ALIAS), except the
+ *     exact in-place form out == x of mhc_post.
+ *   - The library keeps no state between calls.  The workspace (see
+ *     mhc_workspace_bytes) is scratch for one call at a time: calls that may
+ *     run concurrently need separate workspaces.
+ */
+#ifndef MHC_H
+#define MHC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_HC_MULT 4          /* residual streams n */
+#define MHC_NUM_LOGITS 24      /* 2n + n*n: pre-mix | post | comb (row-major) */
+#define MHC_MAX_TOKENS (1 << 22)
+
+typedef enum {
+    MHC_OK = 0,
+    MHC_ERR_NULL = 1,        /* a required pointer is NULL */
+    MHC_ERR_SHAPE = 2,       /* T < 0 or too large, eps < 0 or not finite, sinkhorn_iters < 1 */
+    MHC_ERR_UNSUPPORTED = 3, /* n != 4, or C outside the supported set */
+    MHC_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    MHC_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
+    MHC_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than mhc_workspace_bytes */
+    MHC_ERR_HIP = 7          /* the HIP runtime refused the launch (e.g. no device) */
+} mhc_status;
+
+/* Weights of one seam.
+ *   fn_packed: the projection weight fn[K][24] (K = n*C, or C for the entry
+ *              seam) in the library's packed form, produced once per weight by
+ *              mhc_pack_fn.  p1 Approach: "projection against fn".
+ *   bias:      [24] float, added to the logits.
+ *   alpha:     [3] float, scale of the pre-mix, post and comb logit groups.
+ * Logit j of a token is alpha[g(j)] * (r * P_j) + bias[j], with P = x . fn,
+ * r = 1/sqrt(mean(x^2) + eps) over the K row elements and g(j) = 0 for j < 4,
+ * 1 for 4 <= j < 8, 2 otherwise. */
+typedef struct {
+    const void *fn_packed;
+    const float *bias;
+    const float *alpha;
+} mhc_weights;
+
+/* Bytes of the packed projection weight for K rows (K a multiple of 32):
+ * 96*K, the same as the float32 weight. */
+size_t mhc_fn_packed_bytes(int K);
+
+/* Pack fn[K][24] (float32, device) into fn_packed (device, mhc_fn_packed_bytes(K)
+ * bytes): each weight is split into a bf16 pair hi + lo (hi = bf16(f),
+ * lo = bf16(f - hi); |f - hi - lo| <= 2^-18 |f|) and laid out in the operand
+ * order of the gfx950 bf16 matrix instructions.  Run once per weight, not per
+ * call.  K must be a multiple of 32 and at most 4*16384. */
+mhc_status mhc_pack_fn(const float *fn, int K, void *fn_packed, void *stream);
+
+/* Workspace bytes needed by mhc_pre, mhc_pre_delayed and mhc_broadcast_entry
+ * for any T <= T_max with this n and C (small token counts split the
+ * projection over workgroups and combine partial sums in it).  The caller
+ * zero-fills the workspace once after allocating it; every call leaves its
+ * counters back at zero, so it can be reused (and captured) without clearing. */
+size_t mhc_workspace_bytes(int T_max, int n, int C);
+
+/* Pre stage, seam collapsed with its own pre-mix (p1 Purpose: the V4 form).
+ *   x           [T][n][C] bf16    residual streams.
+ *   norm_weight [C] bf16 or NULL  NULL: layer_input = bf16(y).  Otherwise the
+ *                                 folded RMSNorm of p3 Measurements:
+ *                                 layer_input = bf16((y * ry) * w), ry =
+ *                                 1/sqrt(mean(y^2) + eps), evaluated in float
+ *                                 and rounded once.
+ *   eps         >= 0, used in the RMS of the projection and of the norm.
+ *   sinkhorn_iters >= 1 rounds of (row normalise, column normalise) on
+ *               exp(comb logits) (p1 Summary: 20 iterations).
+ *   pre  [T][n]    float out  sigmoid(l[0:4])
+ *   post [T][n]    float out  2*sigmoid(l[4:8]), in (0,2)
+ *   comb [T][n][n] float out  Sinkhorn(exp(l[8:24])), column sums 1
+ *   layer_input [T][C] bf16 out  y_c = sum_i pre_i x_{i,c}, each product
+ *               rounded to float and summed over i = 0..3 left to right. */
+mhc_status mhc_pre(const uint16_t *x, int T, int n, int C, mhc_weights w,
+                   const uint16_t *norm_weight, float eps, int sinkhorn_iters,
+                   float *pre, float *post, float *comb, uint16_t *layer_input,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Pre stage of the delayed (V4.1) seam, p1 Purpose: the streams are collapsed
+ * with the PREVIOUS seam's pre-mix pre_in[T][n] (float, device), and this
+ * seam's pre-mix is returned in pre_out for the next seam.  The projection,
+ * RMS, gates and Sinkhorn are those of mhc_pre (p1 Purpose: only the collapse
+ * differs); so is everything else above. */
+mhc_status mhc_pre_delayed(const uint16_t *x, const float *pre_in, int T, int n,
+                           int C, mhc_weights w, const uint16_t *norm_weight,
+                           float eps, int sinkhorn_iters, float *pre_out,
+                           float *post, float *comb, uint16_t *layer_input,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Post stage (p1 Result, the mhc_post call sites):
+ *   out[t][i][c] = bf16(post[t][i] * y[t][c] + sum_j comb[t][i][j] * x[t][j][c])
+ * evaluated in float, rounded once.  y [T][C] bf16 is the sublayer output,
+ * x [T][n][C] bf16 the residual, post [T][n] and comb [T][n][n] float from
+ * the pre stage.  out [T][n][C] bf16 may be exactly x (in place); any other
+ * overlap is MHC_ERR_ALIAS.  No workspace. */
+mhc_status mhc_post(const uint16_t *y, const uint16_t *x, const float *post,
+                    const float *comb, int T, int n, int C, uint16_t *out,
+                    void *stream);
+
+/* Model-entry seam (p1 Summary and Approach: the broadcast seam projects a
+ * narrower operand).  The single stream h[T][C] bf16 is broadcast to all n
+ * streams, x_out[t][i][:] = h[t][:]; the logits come from h . fn_e with the
+ * entry weight fn_e[C][24] (packed with K = C) and r = 1/sqrt(mean(h^2) + eps)
+ * over C, which equals the RMS of the broadcast row.  Gates, Sinkhorn and the
+ * collapse (with this seam's own pre-mix) are those of mhc_pre applied to
+ * x_out.  layer_input may be NULL (not written).  pre is carried into the
+ * first delayed seam. */
+mhc_status mhc_broadcast_entry(const uint16_t *h, int T, int n, int C,
+                               mhc_weights w_entry, const uint16_t *norm_weight,
+                               float eps, int sinkhorn_iters, uint16_t *x_out,
+                               float *pre, float *post, float *comb,
+                               uint16_t *layer_input, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *mhc_status_str(mhc_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MHC_H */

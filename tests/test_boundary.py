@@ -1,0 +1,179 @@
+"""The C-ABI boundary on the CPU (no GPU): the library loads, exports every
+entry point that include/mhc.h declares, and its host-side validation returns
+the documented status before any kernel is enqueued.  Pointers here are fake
+device addresses; validation never dereferences them."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_mhc_pre_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WS, HIP = range(8)
+T, C = 8, 5120
+MiB = 1 << 20
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhc_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_exports():
+    assert _declared() == sorted(m.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = m.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_sizes():
+    assert m.mhc_fn_packed_bytes(4 * C) == 4 * C * 24 * 4
+    assert m.mhc_fn_packed_bytes(0) == 0
+    assert m.mhc_workspace_bytes(1, 4, C) > 0
+    # large token counts use whole tiles per workgroup: the bound does not grow with T
+    assert m.mhc_workspace_bytes(1 << 20, 4, C) == m.mhc_workspace_bytes(4096, 4, C)
+    assert m.mhc_workspace_bytes(1 << 20, 4, C) < 2 * MiB
+    assert m.mhc_workspace_bytes(16, 3, C) == 0
+    assert m.mhc_workspace_bytes(16, 4, 5000) == 0
+    for s in range(8):
+        assert m.mhc_status_str(s).startswith(m.STATUS[s])
+
+
+class Ptrs:
+    """Distinct, 16-byte aligned fake device addresses, far apart."""
+    def __init__(self):
+        self.next = 0x100000000
+
+    def __call__(self, size=64 * MiB):
+        p = self.next
+        self.next += ((size + 0xFFFFF) // 0x100000) * 0x100000 + 0x100000
+        return p
+
+
+def _pre_args(**kw):
+    P = Ptrs()
+    a = dict(x=P(), pre_in=P(), T=T, n=4, C=C, w=m._Weights(P(), P(), P()), nw=P(), eps=1e-6, iters=20,
+             pre=P(), post=P(), comb=P(), li=P(), ws=P(), ws_bytes=m.mhc_workspace_bytes(T, 4, C))
+    a.update(kw)
+    return a
+
+
+def call_delayed(**kw):
+    a = _pre_args(**kw)
+    return m.lib().mhc_pre_delayed(a["x"], a["pre_in"], a["T"], a["n"], a["C"], a["w"], a["nw"], a["eps"],
+                                   a["iters"], a["pre"], a["post"], a["comb"], a["li"], a["ws"],
+                                   a["ws_bytes"], None)
+
+
+def call_pre(**kw):
+    a = _pre_args(**kw)
+    return m.lib().mhc_pre(a["x"], a["T"], a["n"], a["C"], a["w"], a["nw"], a["eps"], a["iters"],
+                           a["pre"], a["post"], a["comb"], a["li"], a["ws"], a["ws_bytes"], None)
+
+
+def call_entry(**kw):
+    a = _pre_args(**kw)
+    xo = a.get("xo", Ptrs().__call__() + (1 << 40))
+    return m.lib().mhc_broadcast_entry(a["x"], a["T"], a["n"], a["C"], a["w"], a["nw"], a["eps"], a["iters"],
+                                       xo, a["pre"], a["post"], a["comb"], a["li"], a["ws"], a["ws_bytes"],
+                                       None)
+
+
+@pytest.mark.parametrize("call", [call_pre, call_delayed, call_entry])
+def test_pre_validation(call):
+    assert call(n=3) == UNSUP
+    assert call(C=5000) == UNSUP
+    assert call(C=128) == UNSUP
+    assert call(C=16384 + 256) == UNSUP
+    assert call(T=-1) == SHAPE
+    assert call(T=(1 << 22) + 1) == SHAPE
+    assert call(eps=-1e-6) == SHAPE
+    assert call(eps=float("nan")) == SHAPE
+    assert call(eps=float("inf")) == SHAPE
+    assert call(iters=0) == SHAPE
+    assert call(x=None) == NULL
+    assert call(pre=None) == NULL
+    assert call(comb=None) == NULL
+    assert call(w=m._Weights(None, 0x100, 0x200)) == NULL
+    assert call(x=0x100000008) == ALIGN
+    assert call(comb=0x7000000004) == ALIGN
+    assert call(ws_bytes=16) == WS
+    assert call(ws=None) == WS
+    assert call(T=0) == OK              # no-op, nothing launched
+    assert call(T=0, ws=None) == OK
+
+
+def test_delayed_specific():
+    assert call_delayed(pre_in=None) == NULL
+    assert call_delayed(li=None) == NULL
+    # layer_input overlapping x
+    P = Ptrs()
+    x = P()
+    assert call_delayed(x=x, li=x + T * 4 * C * 2 - 16) == ALIAS
+    assert call_delayed(x=x, li=x + T * 4 * C * 2) != ALIAS   # adjacent is fine (then: no GPU)
+    # outputs overlapping each other or the workspace
+    pre = P()
+    assert call_delayed(pre=pre, post=pre + 16) == ALIAS
+    assert call_delayed(pre=pre, ws=pre) == ALIAS
+    # pre_out must not overlap the carried pre_in
+    assert call_delayed(pre_in=pre, pre=pre) == ALIAS
+
+
+def test_entry_specific():
+    assert call_entry(xo=None) == NULL
+    assert call_entry(li=None, ws=None, T=0) == OK       # layer_input is optional
+    P = Ptrs()
+    h = P()
+    assert call_entry(x=h, xo=h + 32) == ALIAS
+
+
+def test_large_tokens_need_no_workspace():
+    # T >= 4096: one workgroup per 16-token tile, nothing to combine.  Validation
+    # passes with no workspace; the launch then fails only for lack of a GPU.
+    assert call_delayed(T=4096, ws=None) == HIP
+
+
+def test_valid_call_reaches_the_runtime():
+    assert call_delayed() == HIP
+    assert call_pre() == HIP
+
+
+def _post(y, x, post, comb, T_, n, C_, out):
+    return m.lib().mhc_post(y, x, post, comb, T_, n, C_, out, None)
+
+
+def test_post_validation():
+    P = Ptrs()
+    y, x, po, cb, out = P(), P(), P(), P(), P()
+    assert _post(y, x, po, cb, T, 3, C, out) == UNSUP
+    assert _post(y, x, po, cb, T, 4, 1000, out) == UNSUP
+    assert _post(y, x, po, cb, -2, 4, C, out) == SHAPE
+    assert _post(None, x, po, cb, T, 4, C, out) == NULL
+    assert _post(y, x, po, cb, T, 4, C, None) == NULL
+    assert _post(y + 2, x, po, cb, T, 4, C, out) == ALIGN
+    assert _post(y, x, po, cb, T, 4, C, x + 1024) == ALIAS        # partial overlap with x
+    assert _post(y, x, po, cb, T, 4, C, y) == ALIAS               # over the sublayer output
+    assert _post(y, x, po, cb, T, 4, C, po) == ALIAS
+    assert _post(y, x, po, cb, 0, 4, C, x) == OK                  # exact in place, T = 0: no-op
+    assert _post(y, x, po, cb, T, 4, C, x) == HIP                 # exact in place is legal
+    assert _post(y, x, po, cb, T, 4, C, out) == HIP
+
+
+def test_pack_validation():
+    L = m.lib()
+    P = Ptrs()
+    assert L.mhc_pack_fn(None, 4 * C, P(), None) == NULL
+    assert L.mhc_pack_fn(P(), 100, P(), None) == SHAPE
+    assert L.mhc_pack_fn(P(), 0, P(), None) == SHAPE
+    assert L.mhc_pack_fn(P() + 4, 4 * C, P(), None) == ALIGN
+    f = P()
+    assert L.mhc_pack_fn(f, 4 * C, f + 4096, None) == ALIAS
+    assert L.mhc_pack_fn(P(), 4 * C, P(), None) == HIP

@@ -1,0 +1,266 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small sizes run the oracle on every token (several 16-token tiles and a ragged
+tail); the full configuration sizes run the GPU on all tokens and the oracle on
+sampled rows (tokens are independent).  Bars are in tests/gpu_util.py.
+"""
+import numpy as np
+import pytest
+
+import decode_mhc_pre_amd as M
+import mhc_inputs as mi
+import oracle
+from gpu_util import (check_bf16, check_gates, dev_bf16, dev_f32, host_bits, host_f32,
+                      rms_over_weight, say, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+C = mi.HIDDEN
+
+
+def weights(d):
+    return M.make_weights(dev_f32(d["fn"]), dev_f32(d["bias"]), dev_f32(d["alpha"]))
+
+
+def run_delayed(d, rows=None):
+    x = dev_bf16(d["x"])
+    w = weights(d)
+    nw = dev_bf16(d["norm_weight"]) if d["norm_weight"] is not None else None
+    pre_out, post, comb, li = M.mhc_pre_delayed(x, dev_f32(d["pre_in"]), w, nw, d["eps"], d["iters"])
+    torch_mod().cuda.synchronize()
+    r = slice(None) if rows is None else rows
+    return (host_f32(pre_out)[r], host_f32(post)[r], host_f32(comb)[r], host_bits(li)[r])
+
+
+def oracle_delayed(d, rows=None):
+    r = slice(None) if rows is None else rows
+    return oracle.mhc_pre_delayed(d["x"][r], d["pre_in"][r], d["fn"], d["bias"], d["alpha"], d["eps"],
+                                  d["iters"], norm_weight=d["norm_weight"])
+
+
+# ----------------------------------------------------------------------------- packing
+
+def test_pack_fn_split_and_layout():
+    """Packed weight = nearest-even bf16 hi plus bf16 of the remainder, in the
+    documented MFMA operand order."""
+    torch = torch_mod()
+    rng = np.random.default_rng(21)
+    K = 4 * 256
+    fn = (rng.standard_normal((K, 24)) * 0.02).astype(np.float32)
+    packed = M.mhc_pack_fn(dev_f32(fn))
+    torch.cuda.synchronize()
+    pk = packed.cpu().numpy().view(np.uint16).reshape(K // 32, 3, 64, 8)
+    # decode: lane L of tile q holds column 16q + (L & 15), rows 32 kb + 8 (L >> 4) + e
+    cols = np.zeros((K, 48), dtype=np.uint16)
+    for q in range(3):
+        for L in range(64):
+            for e in range(8):
+                cols[np.arange(K // 32) * 32 + 8 * (L >> 4) + e, 16 * q + (L & 15)] = pk[:, q, L, e]
+    hi = oracle.bf16_to_f64(cols[:, :24])
+    lo = oracle.bf16_to_f64(cols[:, 24:])
+    f = fn.astype(np.float64)
+    assert np.array_equal(cols[:, :24], oracle.bf16_rne(f))
+    assert np.array_equal(cols[:, 24:], oracle.bf16_rne(f - hi))
+    assert np.all(np.abs(f - hi - lo) <= 2.0 ** -18 * np.abs(f))
+
+
+# ----------------------------------------------------------------------------- pre, delayed, entry
+
+@pytest.mark.parametrize("T", [1, 2, 7, 8, 17, 128, 1000])
+def test_pre_no_norm(T):
+    """Configuration 0 (T = 8, no norm) and neighbours: own pre-mix."""
+    d = mi.pre_inputs(T, seed=100 + T)
+    x = dev_bf16(d["x"])
+    pre, post, comb, li = M.mhc_pre(x, weights(d), None, d["eps"], d["iters"])
+    o = oracle.mhc_pre(d["x"], d["fn"], d["bias"], d["alpha"], d["eps"], d["iters"])
+    say("mhc_pre T=%d no norm" % T)
+    ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"])
+    check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="layer_input")
+
+
+@pytest.mark.parametrize("T", [1, 8, 33, 128])
+def test_pre_with_norm(T):
+    d = mi.pre_inputs(T, seed=200 + T, norm=True)
+    pre, post, comb, li = M.mhc_pre(dev_bf16(d["x"]), weights(d), dev_bf16(d["norm_weight"]), d["eps"],
+                                    d["iters"])
+    o = oracle.mhc_pre(d["x"], d["fn"], d["bias"], d["alpha"], d["eps"], d["iters"],
+                       norm_weight=d["norm_weight"])
+    say("mhc_pre T=%d norm" % T)
+    ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"])
+    check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="layer_input")
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 16, 128, 1024])
+def test_delayed_no_norm_bit_exact_collapse(T):
+    """The pages' token list 1/2/7/128/1024: collapse with the carried pre-mix is bit-exact."""
+    d = mi.pre_inputs(T, seed=300 + T, delayed=True)
+    pre_out, post, comb, li = run_delayed(d)
+    y32 = oracle.collapse32(d["x"], d["pre_in"])
+    assert np.array_equal(li, mi.f32_to_bf16_bits(y32))
+    o = oracle_delayed(d)
+    say("mhc_pre_delayed T=%d no norm" % T)
+    check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"])
+    check_bf16(li, o["li_val"], o["li_mag"], what="layer_input")
+
+
+@pytest.mark.parametrize("T", [1, 5, 128, 300])
+def test_delayed_with_norm(T):
+    """Configuration 1 (T = 128, fused RMSNorm) and ragged neighbours."""
+    d = mi.pre_inputs(T, seed=400 + T, delayed=True, norm=True)
+    pre_out, post, comb, li = run_delayed(d)
+    o = oracle_delayed(d)
+    say("mhc_pre_delayed T=%d norm" % T)
+    check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"])
+    check_bf16(li, o["li_val"], o["li_mag"], what="layer_input")
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 256, 1024])
+def test_unit_rms_of_fused_norm(T):
+    """With weight 1 the folded norm has RMS sqrt(ms/(ms+eps)) ~ 1 per row; a
+    half-wave sum of squares would show the page's sqrt(2) (token counts from
+    the wavefront-bug PR, The bug)."""
+    d = mi.pre_inputs(T, seed=500 + T, delayed=True, norm=True)
+    d["norm_weight"] = np.full(C, 0x3F80, np.uint16)
+    _, _, _, li = run_delayed(d)
+    ratio = rms_over_weight(li, d["norm_weight"])
+    say("unit RMS T=%d: min %.6f max %.6f" % (T, ratio.min(), ratio.max()))
+    assert np.all(np.abs(ratio - 1.0) < 2.0 ** -8)
+
+
+def test_delayed_with_own_pre_equals_pre():
+    """Feeding mhc_pre's pre-mix back as pre_in reproduces mhc_pre bitwise; gates are identical
+    (delayed-pre PR, Purpose: only the collapse differs)."""
+    torch = torch_mod()
+    for T, norm in ((7, False), (130, True)):
+        d = mi.pre_inputs(T, seed=600 + T, norm=norm)
+        x = dev_bf16(d["x"])
+        w = weights(d)
+        nw = dev_bf16(d["norm_weight"]) if norm else None
+        pre, post, comb, li = M.mhc_pre(x, w, nw, d["eps"], d["iters"])
+        pre2, post2, comb2, li2 = M.mhc_pre_delayed(x, pre.clone(), w, nw, d["eps"], d["iters"])
+        torch.cuda.synchronize()
+        assert torch.equal(pre, pre2) and torch.equal(post, post2) and torch.equal(comb, comb2)
+        assert torch.equal(li.view(torch.int16), li2.view(torch.int16))
+
+
+def test_collapse_order_golden_on_gpu():
+    """The rounding-order case of tests/golden/collapse_order.txt, on the GPU."""
+    T = 3
+    xv = np.float32([1.0, 2.0 ** -8, 2.0 ** -24, 2.0 ** -24])
+    x32 = np.broadcast_to(xv[None, :, None], (T, 4, C)).copy()
+    d = mi.pre_inputs(T, seed=7, delayed=True)
+    d["x"] = mi.f32_to_bf16_bits(x32)
+    d["pre_in"] = np.ones((T, 4), np.float32)
+    _, _, _, li = run_delayed(d)
+    assert np.all(li == 0x3F80)
+
+
+@pytest.mark.parametrize("T", [1, 16, 100])
+def test_broadcast_entry(T):
+    torch = torch_mod()
+    d = mi.entry_inputs(T, seed=900 + T)
+    h = dev_bf16(d["h"])
+    w = weights(d)
+    x_out, pre, post, comb, li = M.mhc_broadcast_entry(h, w, dev_bf16(d["norm_weight"]), d["eps"],
+                                                      d["iters"])
+    o = oracle.mhc_broadcast_entry(d["h"], d["fn"], d["bias"], d["alpha"], d["eps"], d["iters"],
+                                   norm_weight=d["norm_weight"])
+    say("entry T=%d" % T)
+    assert np.array_equal(host_bits(x_out), o["x_out"])
+    ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"])
+    check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="layer_input")
+    # without layer_input: same gates, x_out still written
+    x2, pre2, _, _, li2 = M.mhc_broadcast_entry(h, w, None, d["eps"], d["iters"], layer_input=False)
+    torch.cuda.synchronize()
+    assert li2 is None and torch.equal(pre, pre2)
+    assert torch.equal(x2.view(torch.int16), x_out.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- post
+
+def post_gates(T, seed=3):
+    p = mi.post_inputs(T, seed=seed)
+    post = (2.0 / (1.0 + np.exp(-p["post_logit"].astype(np.float64)))).astype(np.float32)
+    comb = np.stack([oracle.sinkhorn(np.exp(m.astype(np.float64)), 20) for m in p["comb_logit"]])
+    return p, post, comb.astype(np.float32)
+
+
+@pytest.mark.parametrize("T", [1, 3, 64])
+def test_post_small(T):
+    torch = torch_mod()
+    p, post, comb = post_gates(T, seed=30 + T)
+    y, x = dev_bf16(p["y"]), dev_bf16(p["x"])
+    out = M.mhc_post(y, x, dev_f32(post), dev_f32(comb))
+    o = oracle.mhc_post(p["y"], p["x"], post, comb)
+    say("mhc_post T=%d" % T)
+    check_bf16(host_bits(out), o["out_val"], o["out_mag"], what="out")
+    # exact in-place form gives the same bits
+    M.mhc_post(y, x, dev_f32(post), dev_f32(comb), out=x)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(x), host_bits(out))
+
+
+def test_post_identity():
+    torch = torch_mod()
+    T = 5
+    p, _, _ = post_gates(T)
+    x = dev_bf16(p["x"])
+    eye = np.tile(np.eye(4, dtype=np.float32), (T, 1, 1))
+    out = M.mhc_post(dev_bf16(p["y"]), x, dev_f32(np.zeros((T, 4), np.float32)), dev_f32(eye))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), p["x"])
+
+
+# ----------------------------------------------------------------------------- full sizes, sampled
+
+def _sample_rows(T, outliers, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    rows |= set(outliers[:16].tolist()) | {0, T - 1}
+    return np.array(sorted(rows))
+
+
+def test_config2_prefill_delayed_norm_sampled():
+    """T = 16384, fused norm, 1% outlier rows x100: GPU on all tokens (the
+    benchmark's launch), oracle on sampled rows incl. outliers."""
+    T = 16384
+    d = mi.pre_inputs(T, seed=2, delayed=True, norm=True, outlier_frac=0.01)
+    assert len(d["outliers"]) == 164
+    rows = _sample_rows(T, d["outliers"])
+    pre_out, post, comb, li = run_delayed(d, rows)
+    o = oracle_delayed(d, rows)
+    say("config 2 sampled rows: %d" % len(rows))
+    check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "cfg2")
+    check_bf16(li, o["li_val"], o["li_mag"], what="cfg2 layer_input")
+    y32 = oracle.collapse32(d["x"][rows], d["pre_in"][rows])
+    d2 = dict(d)
+    d2["norm_weight"] = None
+    _, _, _, li_nn = run_delayed(d2, rows)
+    assert np.array_equal(li_nn, mi.f32_to_bf16_bits(y32))
+
+
+def test_config3_post_sampled():
+    T = 16384
+    p, post, comb = post_gates(T, seed=3)
+    out = M.mhc_post(dev_bf16(p["y"]), dev_bf16(p["x"]), dev_f32(post), dev_f32(comb))
+    torch_mod().cuda.synchronize()
+    rows = _sample_rows(T, np.zeros(0, np.int64), n=64, seed=3)
+    ob = host_bits(out)[rows]
+    o = oracle.mhc_post(p["y"][rows], p["x"][rows], post[rows], comb[rows])
+    say("config 3 sampled rows: %d" % len(rows))
+    check_bf16(ob, o["out_val"], o["out_mag"], what="cfg3 out")
+
+
+def test_repeatable_and_workspace_reset():
+    """Split-K runs leave the workspace counters at zero: back-to-back calls on
+    one workspace, with different token counts, give identical bits."""
+    torch = torch_mod()
+    for T in (1, 64, 1):
+        d = mi.pre_inputs(T, seed=700, delayed=True, norm=True)
+        a = run_delayed(d)
+        b = run_delayed(d)
+        for u, v in zip(a, b):
+            assert np.array_equal(u, v)
+    ws = M.workspace(torch.device("cuda"), 1, C)
+    n_cnt = 256
+    assert int(ws[: 4 * n_cnt].view(torch.int32).abs().sum()) == 0
