@@ -79,7 +79,7 @@ size_t mhc_fn_packed_bytes(int K);
 
 /* Pack fn[K][24] (float32, device) into fn_packed (device, mhc_fn_packed_bytes(K)
  * bytes): each weight is split into a bf16 pair hi + lo (hi = bf16(f),
- * lo = bf16(f - hi); |f - hi - lo| <= 2^-18 |f|) and laid out in the operand
+ * lo = bf16(f - hi); |f - hi - lo| <= 2^-16 |f|) and laid out in the operand
  * order of the gfx950 bf16 matrix instructions.  Run once per weight, not per
  * call.  K must be a multiple of 32 and at most 4*16384. */
 mhc_status mhc_pack_fn(const float *fn, int K, void *fn_packed, void *stream);
