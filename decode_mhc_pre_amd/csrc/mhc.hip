@@ -16,18 +16,26 @@ using namespace mhc;
 
 // Projection workgroups aimed for when few tokens: splitting the 4C row over
 // workgroups spreads the (L2/HBM-resident) projection weight over the chip.
-constexpr int kTargetProjGroups = 256;
-constexpr int kMinKBPerSplit = 4;  // one 32-k step per wave at least
+constexpr int kTargetProjGroups = 128;
+constexpr int kMinKBPerSplit = 8;  // two 32-k steps per wave at least
 constexpr int kMaxC = 16384;
+// The fused delayed kernel keeps a 16-token tile's collapsed rows in registers
+// and needs one workgroup per tile: worth it once the tiles fill the chip.
+constexpr int kFusedC = 5120;
+constexpr int kFusedMinT = 2048;
 
 struct Plan {
   int ntile, nsplit, nproj;
+  bool fused;
 };
 
-Plan make_plan(int T, int KB) {
+Plan make_plan(int T, int KB, bool fused_ok) {
   Plan pl;
   pl.ntile = (T + kTileT - 1) / kTileT;
-  int ns = pl.ntile >= kTargetProjGroups ? 1 : (kTargetProjGroups + pl.ntile - 1) / pl.ntile;
+  pl.fused = fused_ok && T >= kFusedMinT;
+  int ns = (pl.fused || pl.ntile >= kTargetProjGroups)
+               ? 1
+               : (kTargetProjGroups + pl.ntile - 1) / pl.ntile;
   int maxs = KB / kMinKBPerSplit;
   if (maxs < 1) maxs = 1;
   if (ns > maxs) ns = maxs;
@@ -123,7 +131,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   if (any_alias(outs, 6, ins, 6)) return MHC_ERR_ALIAS;
 
   if (T == 0) return MHC_OK;
-  const Plan pl = make_plan(T, KB);
+  const Plan pl = make_plan(T, KB, mode == kModeDelayed && C == kFusedC);
   const size_t need = plan_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return MHC_ERR_WORKSPACE;
 
@@ -153,15 +161,19 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 block(kThreads);
+  if (pl.fused) {
+    hipLaunchKernelGGL(mhc_pre_fused_kernel<kFusedC>, dim3(pl.ntile), dim3(kFusedThreads), 0, s, p);
+    return launched();
+  }
   switch (mode) {
     case kModePre:
-      hipLaunchKernelGGL(mhc_pre_kernel<kModePre>, dim3(pl.nproj), block, 0, s, p);
+      hipLaunchKernelGGL(mhc_pre_split_kernel<kModePre>, dim3(pl.nproj), block, 0, s, p);
       break;
     case kModeDelayed:
-      hipLaunchKernelGGL(mhc_pre_kernel<kModeDelayed>, dim3(pl.nproj + T), block, 0, s, p);
+      hipLaunchKernelGGL(mhc_pre_split_kernel<kModeDelayed>, dim3(pl.nproj + T), block, 0, s, p);
       break;
     default:
-      hipLaunchKernelGGL(mhc_pre_kernel<kModeEntry>, dim3(pl.nproj), block, 0, s, p);
+      hipLaunchKernelGGL(mhc_pre_split_kernel<kModeEntry>, dim3(pl.nproj), block, 0, s, p);
       break;
   }
   return launched();
@@ -196,7 +208,7 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
   const int ntile_max = (T_max + kTileT - 1) / kTileT;
   for (int KB : KBs) {
     for (int nt = 1; nt <= ntile_max && nt <= kTargetProjGroups; ++nt) {
-      const Plan pl = make_plan(nt * kTileT, KB);
+      const Plan pl = make_plan(nt * kTileT, KB, false);
       const size_t b = plan_ws_bytes(pl);
       if (b > best) best = b;
     }

@@ -64,6 +64,42 @@ __device__ __forceinline__ f32x4 mfma_bf16(const uint4& a, const uint4& b, f32x4
                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
+// Streaming load of 16 bytes (non-temporal: x is read once, keep the L2 for the weight).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 nt_load16(const void* ptr) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr)));
+}
+
+// ---------------------------------------------------------------- buffer access
+// Raw buffer descriptors: base in SGPRs, per-lane 32-bit offset.  A load whose
+// offset is at or past `bytes` returns zero and such a store is dropped.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) 32-bit buffer, gfx9 family
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+// streaming (non-temporal) variant for data read exactly once
+__device__ __forceinline__ uint4 buf_load16_nt(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
+__device__ __forceinline__ void buf_store16(uint4 v, rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
+}
+
+// ---------------------------------------------------------------- quad shuffles (DPP)
+// Lane l reads lane l^1 / l^2 of its quad; all 64 lanes must be active.
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1,
+                                                               0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E,
+                                                               0xF, 0xF, false));
+}
+
 // ---------------------------------------------------------------- collapse
 // y_c = fl(fl(fl(fl(p0 x0) + fl(p1 x1)) + fl(p2 x2)) + fl(p3 x3)): each product
 // rounded to float, summed left to right over the streams, never fused --

@@ -1,10 +1,14 @@
 // mhc_kernels.hpp -- the seam kernels of libmhc for gfx950.
 //
-//   mhc_pack_fn_kernel   one-time weight packing (bf16 hi/lo split, MFMA order)
-//   mhc_pre_kernel<MODE> pre stage: projection + RMS (bf16 MFMA, split over
-//                        workgroups when few tokens), gates, Sinkhorn, collapse,
-//                        folded RMSNorm.  MODE = own pre-mix / delayed / entry.
-//   mhc_post_kernel      post stage: post_i * y + sum_j comb_ij x_j, streamed.
+//   mhc_pack_fn_kernel          one-time weight packing (bf16 hi/lo split, MFMA order)
+//   mhc_pre_split_kernel<MODE>  pre stage for any T: projection split over
+//                               workgroups (few tokens) or one workgroup per
+//                               16-token tile, last-arriver reduction, gates +
+//                               Sinkhorn, collapse + folded RMSNorm.
+//   mhc_pre_fused_kernel        delayed pre stage for many tokens (C = 5120):
+//                               one sweep over x per 16-token tile; projection,
+//                               both sums of squares, collapse and norm fused.
+//   mhc_post_kernel             post stage: post_i * y + sum_j comb_ij x_j.
 #pragma once
 
 #include "mhc_device.hpp"
@@ -33,6 +37,10 @@ struct PreParams {
   int ntile, nsplit, nproj;
 };
 
+constexpr int kPS = 28;      // LDS row per token: P[0..23], sum x^2 [24], sum y^2 [25]
+constexpr int kJMax = 8;     // k-steps a wave issues together in the split kernel
+constexpr int kRedChunk = 16;  // partials loaded together by the last arriver
+
 // ------------------------------------------------------------------ packing
 // Packed layout: for 32-row block kb and column tile q (0..2, columns 16q..16q+15
 // of [hi 0..23 | lo 0..23]), lane L of a wave holds the 8 values
@@ -57,6 +65,50 @@ __global__ __launch_bounds__(256) void mhc_pack_fn_kernel(const float* __restric
     v[e] = lo ? (f - hi) : hi;          // f - hi is exact in float
   }
   out[gid] = pack8(v);
+}
+
+// ------------------------------------------------------------------ gates + Sinkhorn
+// One full wave handles a 16-token tile: lane L owns token L >> 2 and comb row
+// L & 3 (four entries).  Row sums stay in the lane; column sums are a butterfly
+// over the four lanes of a quad (DPP), so every lane of a column divides by the
+// same bits.  The row maximum is subtracted before exp (removed exactly by the
+// first row step); reciprocals are the hardware's (error <= 1 ulp).
+__device__ __forceinline__ void tile_gates(const PreParams& p, const float (*s_P)[kPS], int t0,
+                                           float (*s_pre)[kNS]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int tt = lane >> 2;
+  const int row = lane & 3;
+  const int tk = t0 + tt;
+  const bool ok = tk < p.T;
+  const float r = 1.0f / sqrtf(s_P[tt][24] / (float)p.K + p.eps);
+  const float ac = p.alpha[2];
+  float m[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m[j] = ac * (r * s_P[tt][8 + 4 * row + j]) + p.bias[8 + 4 * row + j];
+  const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m[j] = expf(m[j] - mx);
+  for (int it = 0; it < p.iters; ++it) {
+    const float inv = __builtin_amdgcn_rcpf((m[0] + m[1]) + (m[2] + m[3]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] *= inv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float c = m[j] + dpp_quad_xor1(m[j]);
+      c = c + dpp_quad_xor2(c);
+      m[j] *= __builtin_amdgcn_rcpf(c);
+    }
+  }
+  const float lp = p.alpha[0] * (r * s_P[tt][row]) + p.bias[row];
+  const float lq = p.alpha[1] * (r * s_P[tt][4 + row]) + p.bias[4 + row];
+  const float pr = 1.0f / (1.0f + expf(-lp));
+  const float po = 2.0f / (1.0f + expf(-lq));
+  s_pre[tt][row] = pr;
+  if (ok) {
+    reinterpret_cast<float4*>(p.comb)[(size_t)tk * 4 + row] = make_float4(m[0], m[1], m[2], m[3]);
+    p.pre[(size_t)tk * kNS + row] = pr;
+    p.post[(size_t)tk * kNS + row] = po;
+  }
 }
 
 // ------------------------------------------------------------------ collapse + norm, one token
@@ -105,16 +157,17 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
   }
 }
 
-// ------------------------------------------------------------------ pre kernel
-// Workgroups [0, nproj): projection tile (16 tokens) x K-split.  The last split
-// of a tile to arrive (counter in the workspace) reduces the partials in split
-// order, computes gates + Sinkhorn and, unless delayed, the collapse.
-// Delayed only: workgroups [nproj, nproj + T) collapse one token each with the
-// carried pre-mix -- independent of the projection, so no wait between them.
+// ------------------------------------------------------------------ pre kernel, split form
+// Workgroups [0, nproj): projection of a 16-token tile over one K-split.  With
+// nsplit > 1 the last split of a tile to arrive (counter in the workspace)
+// sums the partials in split order.  It then runs gates + Sinkhorn and, unless
+// delayed, the collapse.  Delayed only: workgroups [nproj, nproj + T) collapse
+// one token each with the carried pre-mix; they need nothing from the
+// projection, so no workgroup ever waits for another.
 template <int MODE>
-__global__ __launch_bounds__(256) void mhc_pre_kernel(PreParams p) {
+__global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   __shared__ float s_red[4][kTileT][52];   // per-wave partial D (48 cols) + sumsq
-  __shared__ float s_P[kTileT][kPartStride];
+  __shared__ float s_P[kTileT][kPS];
   __shared__ float s_pre[kTileT][kNS];
   __shared__ float s_tmp[4];
   __shared__ int s_last;
@@ -141,29 +194,44 @@ __global__ __launch_bounds__(256) void mhc_pre_kernel(PreParams p) {
   const int kb0 = (int)(((long long)sp * p.KB) / p.nsplit);
   const int kb1 = (int)(((long long)(sp + 1) * p.KB) / p.nsplit);
 
-  // ---- projection over this split's k-blocks: wave w takes kb0 + w, +4, ...
+  // ---- projection over this split's k-blocks: wave w takes kb0 + w, +4, ...,
+  // issuing up to kJMax steps' loads before the first MFMA.
   const uint16_t* xrow = p.x + (size_t)(valid ? tok : 0) * p.K + g * 8;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
   float ssq = 0.f;
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll 2
-  for (int kb = kb0 + wave; kb < kb1; kb += 4) {
-    const uint4 xv = valid ? *reinterpret_cast<const uint4*>(xrow + (size_t)kb * kKB) : zero;
-    const uint4* bp = p.fnp + (size_t)kb * (kFragPerKB * kWave) + lane;
-    const uint4 b0 = bp[0], b1 = bp[kWave], b2 = bp[2 * kWave];
-    ssq += sumsq8(xv);
-    acc0 = mfma_bf16(xv, b0, acc0);
-    acc1 = mfma_bf16(xv, b1, acc1);
-    acc2 = mfma_bf16(xv, b2, acc2);
-    if (MODE == kModeEntry && valid) {
-      // broadcast h to the four streams while it is in registers
-      const size_t c = (size_t)kb * kKB + g * 8;
-      uint4* xo = reinterpret_cast<uint4*>(p.xout + (size_t)tok * kNS * p.C + c);
-      const size_t C8 = (size_t)(p.C >> 3);
-      xo[0] = xv;
-      xo[C8] = xv;
-      xo[2 * C8] = xv;
-      xo[3 * C8] = xv;
+  for (int base = kb0 + wave; base < kb1; base += 4 * kJMax) {
+    uint4 xv[kJMax], b0[kJMax], b1[kJMax], b2[kJMax];
+#pragma unroll
+    for (int j = 0; j < kJMax; ++j) {
+      const int kb = base + 4 * j;
+      if (kb < kb1) {
+        xv[j] = valid ? *reinterpret_cast<const uint4*>(xrow + (size_t)kb * kKB) : zero;
+        const uint4* bp = p.fnp + (size_t)kb * (kFragPerKB * kWave) + lane;
+        b0[j] = bp[0];
+        b1[j] = bp[kWave];
+        b2[j] = bp[2 * kWave];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kJMax; ++j) {
+      const int kb = base + 4 * j;
+      if (kb < kb1) {
+        ssq += sumsq8(xv[j]);
+        acc0 = mfma_bf16(xv[j], b0[j], acc0);
+        acc1 = mfma_bf16(xv[j], b1[j], acc1);
+        acc2 = mfma_bf16(xv[j], b2[j], acc2);
+        if (MODE == kModeEntry && valid) {
+          // broadcast h to the four streams while it is in registers
+          const size_t c = (size_t)kb * kKB + g * 8;
+          uint4* xo = reinterpret_cast<uint4*>(p.xout + (size_t)tok * kNS * p.C + c);
+          const size_t C8 = (size_t)(p.C >> 3);
+          xo[0] = xv[j];
+          xo[C8] = xv[j];
+          xo[2 * C8] = xv[j];
+          xo[3 * C8] = xv[j];
+        }
+      }
     }
   }
   // sum of squares: lanes (g, i) for g = 0..3 hold parts of token i's sum
@@ -214,48 +282,40 @@ __global__ __launch_bounds__(256) void mhc_pre_kernel(PreParams p) {
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    const float* src = p.part + ((size_t)tile * p.nsplit * kTileT + tt) * kPartStride;
-    v0 = 0.f; v1 = 0.f; vs = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) {
-      const float* ps = src + (size_t)s * kTileT * kPartStride;
-      v0 += __builtin_nontemporal_load(ps + q);
-      if (q < 8) v1 += __builtin_nontemporal_load(ps + 16 + q);
-      if (q == 15) vs += __builtin_nontemporal_load(ps + 24);
+    // sum the partials of every split in split order; each (token, value) pair
+    // is one thread, and its loads are issued kRedChunk at a time
+    const float* src = p.part + (size_t)tile * p.nsplit * kTileT * kPartStride;
+    const size_t sstride = (size_t)kTileT * kPartStride;
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int pair = tid + rep * kThreads;
+      if (pair < kTileT * kPartStride) {
+        const int pt = pair / kPartStride;
+        const int pv = pair - pt * kPartStride;
+        float acc = 0.f;
+        if (t0 + pt < p.T) {
+          for (int s0 = 0; s0 < p.nsplit; s0 += kRedChunk) {
+            float v[kRedChunk];
+#pragma unroll
+            for (int u = 0; u < kRedChunk; ++u)
+              v[u] = (s0 + u < p.nsplit) ? __builtin_nontemporal_load(src + (s0 + u) * sstride + pair) : 0.f;
+#pragma unroll
+            for (int u = 0; u < kRedChunk; ++u)
+              if (s0 + u < p.nsplit) acc += v[u];
+          }
+        }
+        s_P[pt][pv] = acc;
+      }
     }
     if (tid == 0) atomicExch(&p.cnt[tile], 0u);  // leave the workspace as found
+  } else {
+    s_P[tt][q] = v0;
+    if (q < 8) s_P[tt][16 + q] = v1;
+    if (q == 15) s_P[tt][24] = vs;
   }
-  s_P[tt][q] = v0;
-  if (q < 8) s_P[tt][16 + q] = v1;
-  if (q == 15) s_P[tt][24] = vs;
   __syncthreads();
 
-  // ---- gates and Sinkhorn: thread (tt, e) owns comb entry e = 4i + j of token tt
-  {
-    const int e = q;
-    const int tk = t0 + tt;
-    const bool ok = tk < p.T;
-    const float r = 1.0f / sqrtf(s_P[tt][24] / (float)p.K + p.eps);
-    const float a_pre = p.alpha[0], a_post = p.alpha[1], a_comb = p.alpha[2];
-    float m = expf(a_comb * (r * s_P[tt][8 + e]) + p.bias[8 + e]);
-    for (int it = 0; it < p.iters; ++it) {
-      float rs = m + __shfl_xor(m, 1);     // row i: lanes differ in bits 0..1
-      rs += __shfl_xor(rs, 2);
-      m = m / rs;
-      float cs = m + __shfl_xor(m, 4);     // column j: lanes differ in bits 2..3
-      cs += __shfl_xor(cs, 8);
-      m = m / cs;
-    }
-    if (ok) p.comb[(size_t)tk * 16 + e] = m;
-    if (e < 4) {
-      const float l = a_pre * (r * s_P[tt][e]) + p.bias[e];
-      const float pr = 1.0f / (1.0f + expf(-l));
-      s_pre[tt][e] = pr;
-      if (ok) p.pre[(size_t)tk * kNS + e] = pr;
-    } else if (e < 8) {
-      const float l = a_post * (r * s_P[tt][e]) + p.bias[e];
-      if (ok) p.post[(size_t)tk * kNS + (e - 4)] = 2.0f / (1.0f + expf(-l));
-    }
-  }
+  if (wave == 0) tile_gates(p, s_P, t0, s_pre);
 
   if (MODE == kModeDelayed || p.li == nullptr) return;
   __syncthreads();
@@ -264,6 +324,138 @@ __global__ __launch_bounds__(256) void mhc_pre_kernel(PreParams p) {
   for (int k = 0; k < nt; ++k)
     collapse_norm_token<MODE == kModeEntry>(p, t0 + k, s_pre[k][0], s_pre[k][1], s_pre[k][2],
                                              s_pre[k][3], &s_tmp[0]);
+}
+
+// ------------------------------------------------------------------ pre kernel, fused delayed form
+// One workgroup (4 waves, one per SIMD) per 16-token tile; hidden size fixed at
+// compile time.  Wave w owns hidden columns [w*C/4, (w+1)*C/4) of all four
+// streams.  Per 32-column block a lane loads 8 bf16 of each stream for one
+// token (the MFMA A operand), so one sweep over x feeds, without re-reading:
+//   - the projection (3 MFMAs per stream against the packed weight),
+//   - the row sum of squares (one MFMA of the fragment with itself: its
+//     diagonal is the per-token sum),
+//   - the exact-order collapse with the carried pre-mix, kept in registers,
+//   - the sum of squares of the collapsed row for the folded RMSNorm.
+// After a workgroup reduction the gates and Sinkhorn run on one wave, then
+// every wave writes its part of layer_input from the registers it kept.
+// All global traffic of the sweep uses buffer instructions on per-tile
+// descriptors: rows past the last token of a ragged tile read as zero and
+// their stores are dropped by the descriptor's range check.
+constexpr int kFusedThreads = 256;  // 4 waves, one per SIMD
+
+template <int kC>
+__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mhc_pre_fused_kernel(PreParams p) {
+  constexpr int kNW = kFusedThreads / kWave;
+  constexpr int kKBC = kC / kKB;          // 32-column blocks per stream
+  constexpr int kCBW = kKBC / kNW;        // blocks per wave
+  constexpr int kRow = kNS * kC * 2;      // bytes of one token's residual row
+  static_assert(kKBC % kNW == 0, "hidden size must split evenly over the waves");
+  __shared__ float s_red[kNW][kTileT][52];
+  __shared__ float s_P[kTileT][kPS];
+  __shared__ float s_pre[kTileT][kNS];
+  __shared__ float s_ry[kTileT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int i = lane & 15;
+  const int g = lane >> 4;
+  const int t0 = blockIdx.x * kTileT;
+  const int nvalid = min(kTileT, p.T - t0);
+  const rsrc_t rx = make_rsrc(p.x + (size_t)t0 * (kNS * kC), nvalid * kRow);
+  const rsrc_t rf = make_rsrc(p.fnp, p.KB * (kFragPerKB * kWave * 16));
+  const rsrc_t rp = make_rsrc(p.pre_in + (size_t)t0 * kNS, nvalid * 16);
+  const int xlane = i * kRow + g * 16;
+  const int flane = lane * 16;
+  const uint4 pv = buf_load16(rp, i * 16, 0);
+  const float p0 = __uint_as_float(pv.x), p1 = __uint_as_float(pv.y);
+  const float p2 = __uint_as_float(pv.z), p3 = __uint_as_float(pv.w);
+
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, as = a0;
+  float ssy = 0.f;
+  float y[kCBW][8];
+#pragma unroll
+  for (int cb = 0; cb < kCBW; ++cb) {
+    const int cbg = wave * kCBW + cb;
+    uint4 xv[kNS];
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) xv[s] = buf_load16_nt(rx, xlane, (s * kC + cbg * kKB) * 2);
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) {
+      const int fo = (s * kKBC + cbg) * (kFragPerKB * kWave * 16);
+      a0 = mfma_bf16(xv[s], buf_load16(rf, flane, fo), a0);
+      a1 = mfma_bf16(xv[s], buf_load16(rf, flane, fo + kWave * 16), a1);
+      a2 = mfma_bf16(xv[s], buf_load16(rf, flane, fo + 2 * kWave * 16), a2);
+      as = mfma_bf16(xv[s], xv[s], as);
+    }
+    collapse8(xv[0], xv[1], xv[2], xv[3], p0, p1, p2, p3, y[cb]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(y[cb][e], y[cb][e], ssy);
+  }
+
+  // diagonal of x.x^T: row 4g + r of lane (g, i) is token i when i == 4g + r
+  float ssx = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (i == 4 * g + r) ssx = as[r];
+  ssy += __shfl_xor(ssy, 16);
+  ssy += __shfl_xor(ssy, 32);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s_red[wave][4 * g + r][i] = a0[r];
+    s_red[wave][4 * g + r][16 + i] = a1[r];
+    s_red[wave][4 * g + r][32 + i] = a2[r];
+  }
+  if ((i >> 2) == g) s_red[wave][i][48] = ssx;
+  if (g == 0) s_red[wave][i][49] = ssy;
+  __syncthreads();
+
+  {
+    // thread (tt, q): P_q and P_{16+q} (hi and lo parts), q = 14: sum x^2, q = 15: sum y^2
+    const int tt = tid >> 4;
+    const int q = tid & 15;
+    float hi = 0.f, lo = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) { hi += s_red[w][tt][q]; lo += s_red[w][tt][kNL + q]; }
+    s_P[tt][q] = hi + lo;
+    if (q < 8) {
+      hi = 0.f; lo = 0.f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) { hi += s_red[w][tt][16 + q]; lo += s_red[w][tt][kNL + 16 + q]; }
+      s_P[tt][16 + q] = hi + lo;
+    } else if (q >= 14) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) sum += s_red[w][tt][48 + (q - 14)];
+      s_P[tt][24 + (q - 14)] = sum;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) tile_gates(p, s_P, t0, s_pre);
+  if (wave == 1 && lane < kTileT)
+    s_ry[lane] = p.nw ? 1.0f / sqrtf(s_P[lane][25] / (float)kC + p.eps) : 1.0f;
+  __syncthreads();
+
+  const float ry = s_ry[i];
+  const rsrc_t rl = make_rsrc(p.li + (size_t)t0 * kC, nvalid * kC * 2);
+  const int llane = i * (kC * 2) + g * 16;
+  const bool norm = p.nw != nullptr;
+#pragma unroll
+  for (int cb = 0; cb < kCBW; ++cb) {
+    const int c = (wave * kCBW + cb) * kKB;
+    float o[8];
+    if (norm) {
+      float w[8];
+      unpack8(*reinterpret_cast<const uint4*>(p.nw + c + g * 8), w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (y[cb][e] * ry) * w[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = y[cb][e];
+    }
+    buf_store16(pack8(o), rl, llane, c * 2);
+  }
 }
 
 // ------------------------------------------------------------------ post kernel
