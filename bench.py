@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the T=1..128 sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU oracle sample time")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -136,7 +138,7 @@ def main():
     post_avg = sum(post_ms) / len(post_ms)
     pb, qb = pre_bytes(T_SEAM), post_bytes(T_SEAM)
     kernels = {
-        "mhc_pre_kernel<delayed>": dict(avg_us=pre_avg * 1e3, alg_bytes=pb,
+        "mhc_pre_group_kernel (delayed, norm)": dict(avg_us=pre_avg * 1e3, alg_bytes=pb,
                                         gbs=pb / (pre_avg * 1e-3) / 1e9),
         "mhc_post_kernel": dict(avg_us=post_avg * 1e3, alg_bytes=qb, gbs=qb / (post_avg * 1e-3) / 1e9),
     }
@@ -148,6 +150,15 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kernels[dom]["frac"], 4),
                 "traffic": traffic}
     seam_gbs = (pb + qb) / (t_total / args.steps) / 1e9
+
+    if args.copy_ref:
+        # a plain copy kernel of known size: reads and writes 512 MiB each
+        src = torch.empty(256 << 20, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------------------------------------------------------- T = 1..128 sweep
     sweep = None

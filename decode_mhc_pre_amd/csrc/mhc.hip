@@ -19,21 +19,26 @@ using namespace mhc;
 constexpr int kTargetProjGroups = 128;
 constexpr int kMinKBPerSplit = 8;  // two 32-k steps per wave at least
 constexpr int kMaxC = 16384;
-// The fused delayed kernel keeps a 16-token tile's collapsed rows in registers
-// and needs one workgroup per tile: worth it once the tiles fill the chip.
-constexpr int kFusedC = 5120;
-constexpr int kFusedMinT = 2048;
+// The grouped delayed kernel keeps a tile's collapsed rows on chip and splits
+// each 64-token tile over a group of workgroups: worth it once the groups fill
+// the chip.
+constexpr int kGroupC = 5120;
+constexpr int kGroupMinT = 2048;
+constexpr int kGroupYL = 16;  // collapsed-row blocks per wave kept in LDS
+constexpr int kGroupD = 4;    // prefetch distance in 32-column blocks
 
 struct Plan {
   int ntile, nsplit, nproj;
-  bool fused;
+  bool group;
+  int gtiles;  // grouped form: 64-token tiles
 };
 
-Plan make_plan(int T, int KB, bool fused_ok) {
+Plan make_plan(int T, int KB, bool group_ok) {
   Plan pl;
   pl.ntile = (T + kTileT - 1) / kTileT;
-  pl.fused = fused_ok && T >= kFusedMinT;
-  int ns = (pl.fused || pl.ntile >= kTargetProjGroups)
+  pl.group = group_ok && T >= kGroupMinT;
+  pl.gtiles = (T + kGT - 1) / kGT;
+  int ns = (pl.group || pl.ntile >= kTargetProjGroups)
                ? 1
                : (kTargetProjGroups + pl.ntile - 1) / pl.ntile;
   int maxs = KB / kMinKBPerSplit;
@@ -46,12 +51,21 @@ Plan make_plan(int T, int KB, bool fused_ok) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace layout for a plan: [counters: ntile u32, padded to 256 B][partials].
-size_t counter_bytes(int ntile) { return align_up((size_t)ntile * sizeof(unsigned), 256); }
+// Workspace layout: [counters, padded to 256 B][partial sums].
+//   split form:   counters [ntile] u32,      partials [ntile][nsplit][16][25] f32
+//   grouped form: counters [gtiles][2] u32,  partials [gtiles][kGR][64][26] f32
+size_t counter_bytes(const Plan& pl) {
+  const size_t n = pl.group ? 2 * (size_t)pl.gtiles : (size_t)pl.ntile;
+  return align_up(n * sizeof(unsigned), 256);
+}
 size_t plan_ws_bytes(const Plan& pl) {
+  if (pl.group)
+    return counter_bytes(pl) + (size_t)pl.gtiles * kGR * kGT * kGPart * sizeof(float);
   if (pl.nsplit <= 1) return 0;
-  return counter_bytes(pl.ntile) +
-         (size_t)pl.ntile * pl.nsplit * kTileT * kPartStride * sizeof(float);
+  return counter_bytes(pl) + (size_t)pl.ntile * pl.nsplit * kTileT * kPartStride * sizeof(float);
+}
+unsigned group_grid(const Plan& pl) {
+  return (unsigned)(kXcds * kGR * ((pl.gtiles + kXcds - 1) / kXcds));
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -131,7 +145,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   if (any_alias(outs, 6, ins, 6)) return MHC_ERR_ALIAS;
 
   if (T == 0) return MHC_OK;
-  const Plan pl = make_plan(T, KB, mode == kModeDelayed && C == kFusedC);
+  const Plan pl = make_plan(T, KB, mode == kModeDelayed && C == kGroupC);
   const size_t need = plan_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return MHC_ERR_WORKSPACE;
 
@@ -148,7 +162,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   p.li = li;
   p.xout = x_out;
   p.cnt = need ? static_cast<unsigned*>(ws) : nullptr;
-  p.part = need ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(pl.ntile)) : nullptr;
+  p.part = need ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(pl)) : nullptr;
   p.eps = eps;
   p.iters = iters;
   p.T = T;
@@ -161,8 +175,9 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 block(kThreads);
-  if (pl.fused) {
-    hipLaunchKernelGGL(mhc_pre_fused_kernel<kFusedC>, dim3(pl.ntile), dim3(kFusedThreads), 0, s, p);
+  if (pl.group) {
+    hipLaunchKernelGGL((mhc_pre_group_kernel<kGroupC, kGroupYL, kGroupD>), dim3(group_grid(pl)),
+                       dim3(kGroupThreads), 0, s, p);
     return launched();
   }
   switch (mode) {
@@ -202,6 +217,7 @@ mhc_status mhc_pack_fn(const float* fn, int K, void* fn_packed, void* stream) {
 
 size_t mhc_workspace_bytes(int T_max, int n, int C) {
   if (n != MHC_HC_MULT || C < 256 || C > kMaxC || C % 256 != 0 || T_max <= 0) return 0;
+  if (T_max > MHC_MAX_TOKENS) T_max = MHC_MAX_TOKENS;
   size_t best = 0;
   // the entry seam (K = C) and the 4-stream seams (K = 4C) may plan differently
   const int KBs[2] = {C / kKB, MHC_HC_MULT * C / kKB};
@@ -212,6 +228,11 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
       const size_t b = plan_ws_bytes(pl);
       if (b > best) best = b;
     }
+  }
+  // the grouped delayed form grows with the token count
+  if (C == kGroupC) {
+    const Plan pl = make_plan(T_max, MHC_HC_MULT * C / kKB, true);
+    if (pl.group && plan_ws_bytes(pl) > best) best = plan_ws_bytes(pl);
   }
   return best;
 }

@@ -64,10 +64,13 @@ __device__ __forceinline__ f32x4 mfma_bf16(const uint4& a, const uint4& b, f32x4
                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
-// Streaming load of 16 bytes (non-temporal: x is read once, keep the L2 for the weight).
+// Streaming (non-temporal) 16-byte load and store, for data touched exactly once.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 nt_load16(const void* ptr) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr)));
+}
+__device__ __forceinline__ void nt_store16(uint4 v, void* ptr) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(ptr));
 }
 
 // ---------------------------------------------------------------- buffer access

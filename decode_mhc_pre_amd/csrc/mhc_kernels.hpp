@@ -5,9 +5,10 @@
 //                               workgroups (few tokens) or one workgroup per
 //                               16-token tile, last-arriver reduction, gates +
 //                               Sinkhorn, collapse + folded RMSNorm.
-//   mhc_pre_fused_kernel        delayed pre stage for many tokens (C = 5120):
-//                               one sweep over x per 16-token tile; projection,
-//                               both sums of squares, collapse and norm fused.
+//   mhc_pre_group_kernel        delayed pre stage for many tokens (C = 5120):
+//                               one sweep over x; a 64-token tile split over a
+//                               group of workgroups on one XCD; projection, both
+//                               sums of squares, collapse and norm fused.
 //   mhc_post_kernel             post stage: post_i * y + sum_j comb_ij x_j.
 #pragma once
 
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(256) void mhc_pack_fn_kernel(const float* __restric
 // same bits.  The row maximum is subtracted before exp (removed exactly by the
 // first row step); reciprocals are the hardware's (error <= 1 ulp).
 __device__ __forceinline__ void tile_gates(const PreParams& p, const float (*s_P)[kPS], int t0,
-                                           float (*s_pre)[kNS]) {
+                                           float (*s_pre)[kNS], bool write = true) {
   const int lane = threadIdx.x & (kWave - 1);
   const int tt = lane >> 2;
   const int row = lane & 3;
@@ -104,7 +105,7 @@ __device__ __forceinline__ void tile_gates(const PreParams& p, const float (*s_P
   const float pr = 1.0f / (1.0f + expf(-lp));
   const float po = 2.0f / (1.0f + expf(-lq));
   s_pre[tt][row] = pr;
-  if (ok) {
+  if (ok && write) {
     reinterpret_cast<float4*>(p.comb)[(size_t)tk * 4 + row] = make_float4(m[0], m[1], m[2], m[3]);
     p.pre[(size_t)tk * kNS + row] = pr;
     p.post[(size_t)tk * kNS + row] = po;
@@ -326,72 +327,175 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
                                              s_pre[k][3], &s_tmp[0]);
 }
 
-// ------------------------------------------------------------------ pre kernel, fused delayed form
-// One workgroup (4 waves, one per SIMD) per 16-token tile; hidden size fixed at
-// compile time.  Wave w owns hidden columns [w*C/4, (w+1)*C/4) of all four
-// streams.  Per 32-column block a lane loads 8 bf16 of each stream for one
-// token (the MFMA A operand), so one sweep over x feeds, without re-reading:
-//   - the projection (3 MFMAs per stream against the packed weight),
-//   - the row sum of squares (one MFMA of the fragment with itself: its
+// ------------------------------------------------------------------ pre kernel, grouped delayed form
+// Many tokens, hidden size fixed at compile time.  A tile of 64 tokens is
+// covered by a group of kGR workgroups; member r owns hidden columns
+// [r*C/kGR, (r+1)*C/kGR) of all four streams, and its wave w owns tokens
+// 16w..16w+15 of the tile.  The four waves walk the same 32-column blocks in
+// step, so each weight fragment is fetched from L2 once per workgroup and
+// served to the other waves from L1: the weight costs 1/64 of its size per
+// token instead of 1/16.  Per block a lane loads 8 bf16 of each stream for
+// one token (the MFMA A operand), so one sweep over x feeds, without
+// re-reading:
+//   - the partial projection (3 MFMAs per stream against the packed weight),
+//   - the partial row sum of squares (MFMA of the fragment with itself: its
 //     diagonal is the per-token sum),
-//   - the exact-order collapse with the carried pre-mix, kept in registers,
-//   - the sum of squares of the collapsed row for the folded RMSNorm.
-// After a workgroup reduction the gates and Sinkhorn run on one wave, then
-// every wave writes its part of layer_input from the registers it kept.
+//   - the exact-order collapse with the carried pre-mix,
+//   - the partial sum of squares of the collapsed row (folded RMSNorm).
+// The collapsed rows stay on chip until the norm factor is known: most blocks
+// in registers, kYL blocks per wave in LDS; the registers this frees hold a
+// rotating prefetch kD blocks deep.  The members then exchange their partial
+// sums through the workspace (group barrier, below), every member reduces them
+// in member order -- the same bits in every member -- and runs gates +
+// Sinkhorn; member 0 writes the gates, every member writes its columns of
+// layer_input.
+//
+// Group barrier.  Blocks are dispatched to the XCDs round-robin (block b on
+// XCD b % 8) and in order within an XCD, so the members of a group -- blocks
+// 8(kGR*j + r) + xcd for r = 0..kGR-1 -- are consecutive in one XCD's order
+// and share its L2: when the last member is dispatched the others are already
+// resident, and the only group that can be partially resident on an XCD is
+// the newest one.  The wait is nevertheless bounded (kSpinMax sleeps, well
+// over a second), so it always ends.  Arrival and departure counters are
+// reset by the last member to leave, so the workspace is left as found.
 // All global traffic of the sweep uses buffer instructions on per-tile
 // descriptors: rows past the last token of a ragged tile read as zero and
 // their stores are dropped by the descriptor's range check.
-constexpr int kFusedThreads = 256;  // 4 waves, one per SIMD
+constexpr int kGroupThreads = 256;   // 4 waves, one per SIMD
+constexpr int kGR = 4;               // workgroups per tile
+constexpr int kGT = 64;              // tokens per tile (16 per wave)
+constexpr int kXcds = 8;
+constexpr int kSpinMax = 1 << 24;
+constexpr int kGPart = 26;           // exchanged per token: P[24], sum x^2, sum y^2
 
-template <int kC>
-__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mhc_pre_fused_kernel(PreParams p) {
-  constexpr int kNW = kFusedThreads / kWave;
+// Partial sums cross workgroups (possibly XCDs) through device-coherent
+// accesses: agent-scope atomic stores and loads, each coherent on its own, so
+// no release fence has to write back the L2 (measured: such a fence cost ~20 us
+// per workgroup here, flushing other workgroups' dirty layer_input lines).  A
+// writer waits for its own stores to complete before the workgroup barrier
+// that precedes the arrival increment.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS-only barrier: waits for this wave's LDS traffic, then s_barrier.  Unlike
+// __syncthreads it does not wait for outstanding global loads, so the
+// prefetched blocks stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int kC, int kYL, int kD>
+__global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mhc_pre_group_kernel(PreParams p) {
+  constexpr int kNW = kGroupThreads / kWave;
   constexpr int kKBC = kC / kKB;          // 32-column blocks per stream
-  constexpr int kCBW = kKBC / kNW;        // blocks per wave
+  constexpr int kCBW = kKBC / kGR;        // blocks per member (all waves walk the same ones)
   constexpr int kRow = kNS * kC * 2;      // bytes of one token's residual row
-  static_assert(kKBC % kNW == 0, "hidden size must split evenly over the waves");
-  __shared__ float s_red[kNW][kTileT][52];
-  __shared__ float s_P[kTileT][kPS];
-  __shared__ float s_pre[kTileT][kNS];
-  __shared__ float s_ry[kTileT];
+  constexpr int kSlots = kD + 1;
+  constexpr int kFrag = kFragPerKB * kWave * 16;  // bytes of one k-block of packed weight
+  static_assert(kKBC % kGR == 0, "hidden size must split evenly over the group");
+  static_assert(kNW * kTileT == kGT, "one 16-token MFMA tile per wave");
+  static_assert(kNW == kNS, "wave w fetches the weight fragments of stream w");
+  static_assert(kYL <= kCBW, "more LDS blocks than blocks");
+  __shared__ float4 s_y[kNW][kYL > 0 ? kYL : 1][2][kWave];  // collapsed rows kept in LDS
+  __shared__ float s_pre[kGT][kNS];
+  __shared__ float s_ry[kGT];
+  __shared__ uint4 s_w[kCBW][4];    // this member's columns of the norm weight (bf16)
+  // the weight block ring (2 x 12 KB) is only live during the sweep; afterwards
+  // the same bytes hold the per-wave partial sums and the reduced tile sums
+  typedef uint4 FnRing[2][kNS][kFragPerKB][kWave];
+  typedef float RedBuf[kNW][kTileT][52];
+  typedef float TileBuf[kGT][kPS];
+  static_assert(sizeof(RedBuf) + sizeof(TileBuf) <= sizeof(FnRing), "reuse of the ring");
+  __shared__ FnRing s_fn;
+  RedBuf& s_red = *reinterpret_cast<RedBuf*>(&s_fn[0][0][0][0]);
+  TileBuf& s_P = *reinterpret_cast<TileBuf*>(reinterpret_cast<char*>(&s_fn[0][0][0][0]) + sizeof(RedBuf));
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int i = lane & 15;
   const int g = lane >> 4;
-  const int t0 = blockIdx.x * kTileT;
-  const int nvalid = min(kTileT, p.T - t0);
+  const int xcd = blockIdx.x % kXcds;
+  const int q = blockIdx.x / kXcds;
+  const int mem = q % kGR;                      // member of the group
+  const int tile = (q / kGR) * kXcds + xcd;
+  const int t0 = tile * kGT;
+  if (t0 >= p.T) return;                        // the whole group agrees
+  const int wt0 = t0 + wave * kTileT;           // this wave's first token
+  // descriptors depend on the block only (they must stay in SGPRs); a lane's
+  // token row within the tile goes into its offset, which the range check covers
+  const int nvalid = min(kGT, p.T - t0);
+  const int tw = wave * kTileT + i;             // the lane's token within the tile
   const rsrc_t rx = make_rsrc(p.x + (size_t)t0 * (kNS * kC), nvalid * kRow);
-  const rsrc_t rf = make_rsrc(p.fnp, p.KB * (kFragPerKB * kWave * 16));
+  const rsrc_t rf = make_rsrc(p.fnp, p.KB * kFrag);
   const rsrc_t rp = make_rsrc(p.pre_in + (size_t)t0 * kNS, nvalid * 16);
-  const int xlane = i * kRow + g * 16;
+  const int xlane = tw * kRow + g * 16;
   const int flane = lane * 16;
-  const uint4 pv = buf_load16(rp, i * 16, 0);
+  const uint4 pv = buf_load16(rp, tw * 16, 0);
   const float p0 = __uint_as_float(pv.x), p1 = __uint_as_float(pv.y);
   const float p2 = __uint_as_float(pv.z), p3 = __uint_as_float(pv.w);
+  const int cb0 = mem * kCBW;                   // first column block of this member
+  if (p.nw && tid < kCBW * 4)
+    s_w[tid >> 2][tid & 3] = reinterpret_cast<const uint4*>(p.nw)[cb0 * 4 + tid];
+  // tiles walk their blocks from different starting points, so that at any
+  // time the chip's x reads spread over many columns (and L2 channels)
+  const int rot = (tile * 7) % kCBW;
+
+  // rotating prefetch: slot k holds block b with b % kSlots == k; per block a
+  // wave fetches its tokens' x (4 streams) and one stream's weight fragments
+  uint4 xq[kSlots][kNS];
+  uint4 fq[kSlots][kFragPerKB];
+  auto issue = [&](int cb, int slot) {
+    int blk = cb + rot;
+    blk = blk >= kCBW ? blk - kCBW : blk;
+    const int cbg = cb0 + blk;
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) xq[slot][s] = buf_load16(rx, xlane, (s * kC + cbg * kKB) * 2);
+#pragma unroll
+    for (int f = 0; f < kFragPerKB; ++f)
+      fq[slot][f] = buf_load16(rf, flane, (wave * kKBC + cbg) * kFrag + f * kWave * 16);
+  };
+#pragma unroll
+  for (int d = 0; d < kD; ++d) issue(d, d);
 
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, as = a0;
   float ssy = 0.f;
-  float y[kCBW][8];
+  float y[kCBW - kYL][8];
 #pragma unroll
   for (int cb = 0; cb < kCBW; ++cb) {
-    const int cbg = wave * kCBW + cb;
-    uint4 xv[kNS];
+    if (cb + kD < kCBW) issue(cb + kD, (cb + kD) % kSlots);
+    const int slot = cb % kSlots;
+    // publish this wave's stream of the weight block, then read all four
 #pragma unroll
-    for (int s = 0; s < kNS; ++s) xv[s] = buf_load16_nt(rx, xlane, (s * kC + cbg * kKB) * 2);
+    for (int f = 0; f < kFragPerKB; ++f) s_fn[cb & 1][wave][f][lane] = fq[slot][f];
+    lds_barrier();
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
-      const int fo = (s * kKBC + cbg) * (kFragPerKB * kWave * 16);
-      a0 = mfma_bf16(xv[s], buf_load16(rf, flane, fo), a0);
-      a1 = mfma_bf16(xv[s], buf_load16(rf, flane, fo + kWave * 16), a1);
-      a2 = mfma_bf16(xv[s], buf_load16(rf, flane, fo + 2 * kWave * 16), a2);
-      as = mfma_bf16(xv[s], xv[s], as);
+      a0 = mfma_bf16(xq[slot][s], s_fn[cb & 1][s][0][lane], a0);
+      a1 = mfma_bf16(xq[slot][s], s_fn[cb & 1][s][1][lane], a1);
+      a2 = mfma_bf16(xq[slot][s], s_fn[cb & 1][s][2][lane], a2);
+      as = mfma_bf16(xq[slot][s], xq[slot][s], as);
     }
-    collapse8(xv[0], xv[1], xv[2], xv[3], p0, p1, p2, p3, y[cb]);
+    float yb[8];
+    collapse8(xq[slot][0], xq[slot][1], xq[slot][2], xq[slot][3], p0, p1, p2, p3, yb);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(y[cb][e], y[cb][e], ssy);
+    for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(yb[e], yb[e], ssy);
+    if (cb < kYL) {
+      s_y[wave][cb][0][lane] = make_float4(yb[0], yb[1], yb[2], yb[3]);
+      s_y[wave][cb][1][lane] = make_float4(yb[4], yb[5], yb[6], yb[7]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[cb - kYL][e] = yb[e];
+    }
   }
 
   // diagonal of x.x^T: row 4g + r of lane (g, i) is token i when i == 4g + r
@@ -401,6 +505,7 @@ void mhc_pre_fused_kernel(PreParams p) {
     if (i == 4 * g + r) ssx = as[r];
   ssy += __shfl_xor(ssy, 16);
   ssy += __shfl_xor(ssy, 32);
+  __syncthreads();  // every wave is done with the weight ring
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     s_red[wave][4 * g + r][i] = a0[r];
@@ -411,48 +516,88 @@ void mhc_pre_fused_kernel(PreParams p) {
   if (g == 0) s_red[wave][i][49] = ssy;
   __syncthreads();
 
+  // ---- publish this member's partials: token (wave, tt), values 6*part .. 6*part+5
+  float* part = p.part + (size_t)tile * kGR * kGT * kGPart;
   {
-    // thread (tt, q): P_q and P_{16+q} (hi and lo parts), q = 14: sum x^2, q = 15: sum y^2
-    const int tt = tid >> 4;
-    const int q = tid & 15;
-    float hi = 0.f, lo = 0.f;
+    const int tt = lane >> 2, pp = lane & 3;
+    float* dst = part + ((size_t)mem * kGT + wave * kTileT + tt) * kGPart;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) { hi += s_red[w][tt][q]; lo += s_red[w][tt][kNL + q]; }
-    s_P[tt][q] = hi + lo;
-    if (q < 8) {
-      hi = 0.f; lo = 0.f;
-#pragma unroll
-      for (int w = 0; w < kNW; ++w) { hi += s_red[w][tt][16 + q]; lo += s_red[w][tt][kNL + 16 + q]; }
-      s_P[tt][16 + q] = hi + lo;
-    } else if (q >= 14) {
-      float sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < kNW; ++w) sum += s_red[w][tt][48 + (q - 14)];
-      s_P[tt][24 + (q - 14)] = sum;
+    for (int u = 0; u < 6; ++u) {
+      const int j = pp * 6 + u;
+      st_agent(dst + j, s_red[wave][tt][j] + s_red[wave][tt][kNL + j]);
+    }
+    if (pp < 2) st_agent(dst + kNL + pp, s_red[wave][tt][48 + pp]);
+  }
+  wait_stores();
+  __syncthreads();
+  unsigned* arrive = p.cnt + 2 * tile;
+  unsigned* depart = arrive + 1;
+  if (tid == 0) {
+    __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int spins = 0;
+    while (ld_agent(arrive) < (unsigned)kGR && spins < kSpinMax) {
+      __builtin_amdgcn_s_sleep(2);
+      ++spins;
     }
   }
   __syncthreads();
-  if (wave == 0) tile_gates(p, s_P, t0, s_pre);
-  if (wave == 1 && lane < kTileT)
-    s_ry[lane] = p.nw ? 1.0f / sqrtf(s_P[lane][25] / (float)kC + p.eps) : 1.0f;
+  {
+    // sum the members' partials in member order: token tid >> 2, values of part tid & 3
+    const int tt = tid >> 2, pp = tid & 3;
+    const int nj = pp < 2 ? 7 : 6;  // parts 0/1 also carry sum x^2 / sum y^2
+#pragma unroll
+    for (int u = 0; u < 7; ++u) {
+      if (u < nj) {
+        const int j = u < 6 ? pp * 6 + u : kNL + pp;
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < kGR; ++m)
+          acc += ld_agent(part + ((size_t)m * kGT + tt) * kGPart + j);
+        s_P[tt][j] = acc;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0 && atomicAdd(depart, 1u) == (unsigned)(kGR - 1)) {
+    atomicExch(arrive, 0u);  // every member has passed the barrier: reset for the next call
+    atomicExch(depart, 0u);
+  }
+
+  // ---- gates (member 0 writes them) and norm factor, each wave its 16 tokens
+  tile_gates(p, &s_P[wave * kTileT], wt0, &s_pre[wave * kTileT], mem == 0);
+  if (lane < kTileT) {
+    const int tt = wave * kTileT + lane;
+    s_ry[tt] = p.nw ? 1.0f / sqrtf(s_P[tt][25] / (float)kC + p.eps) : 1.0f;
+  }
   __syncthreads();
 
-  const float ry = s_ry[i];
+  const float ry = s_ry[tw];
   const rsrc_t rl = make_rsrc(p.li + (size_t)t0 * kC, nvalid * kC * 2);
-  const int llane = i * (kC * 2) + g * 16;
+  const int llane = tw * (kC * 2) + g * 16;
   const bool norm = p.nw != nullptr;
 #pragma unroll
   for (int cb = 0; cb < kCBW; ++cb) {
-    const int c = (wave * kCBW + cb) * kKB;
+    int blk = cb + rot;
+    blk = blk >= kCBW ? blk - kCBW : blk;
+    const int c = (cb0 + blk) * kKB;
+    float yb[8];
+    if (cb < kYL) {
+      const float4 u = s_y[wave][cb][0][lane], v = s_y[wave][cb][1][lane];
+      yb[0] = u.x; yb[1] = u.y; yb[2] = u.z; yb[3] = u.w;
+      yb[4] = v.x; yb[5] = v.y; yb[6] = v.z; yb[7] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yb[e] = y[cb - kYL][e];
+    }
     float o[8];
     if (norm) {
       float w[8];
-      unpack8(*reinterpret_cast<const uint4*>(p.nw + c + g * 8), w);
+      unpack8(s_w[c / kKB - cb0][g], w);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (y[cb][e] * ry) * w[e];
+      for (int e = 0; e < 8; ++e) o[e] = (yb[e] * ry) * w[e];
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = y[cb][e];
+      for (int e = 0; e < 8; ++e) o[e] = yb[e];
     }
     buf_store16(pack8(o), rl, llane, c * 2);
   }
@@ -460,8 +605,10 @@ void mhc_pre_fused_kernel(PreParams p) {
 
 // ------------------------------------------------------------------ post kernel
 // One thread per (token, 8 hidden elements): reads y (16 B) and the four
-// streams (4 x 16 B), writes four streams.  Exact in-place (out == x) is safe:
-// a thread reads all of its x before it writes.
+// streams (4 x 16 B), writes four streams.  Every byte is touched once, so all
+// traffic is non-temporal (streaming): measured ~14% faster than cached
+// accesses at T = 16384.  Exact in-place (out == x) is safe: a thread reads
+// all of its x before it writes.
 __global__ __launch_bounds__(256) void mhc_post_kernel(const uint4* __restrict__ y,
                                                        const uint4* x,
                                                        const float* __restrict__ post,
@@ -471,18 +618,22 @@ __global__ __launch_bounds__(256) void mhc_post_kernel(const uint4* __restrict__
   if (idx >= (long long)T * C8) return;
   const int t = (int)(idx / C8);
   const int c8 = (int)(idx - (long long)t * C8);
+  const size_t xb = (size_t)t * kNS * C8 + c8;
+  const uint4 yq = nt_load16(y + (size_t)t * C8 + c8);
+  const uint4 q0 = nt_load16(x + xb);
+  const uint4 q1 = nt_load16(x + xb + C8);
+  const uint4 q2 = nt_load16(x + xb + 2 * (size_t)C8);
+  const uint4 q3 = nt_load16(x + xb + 3 * (size_t)C8);
   const float4 pg = reinterpret_cast<const float4*>(post)[t];
   const float4* cb = reinterpret_cast<const float4*>(comb) + (size_t)t * 4;
-  const float4 c0 = cb[0], c1 = cb[1], c2 = cb[2], c3 = cb[3];
-  const size_t xb = (size_t)t * kNS * C8 + c8;
+  const float4 cr[4] = {cb[0], cb[1], cb[2], cb[3]};
   float yv[8], x0[8], x1[8], x2[8], x3[8];
-  unpack8(y[(size_t)t * C8 + c8], yv);
-  unpack8(x[xb], x0);
-  unpack8(x[xb + C8], x1);
-  unpack8(x[xb + 2 * (size_t)C8], x2);
-  unpack8(x[xb + 3 * (size_t)C8], x3);
+  unpack8(yq, yv);
+  unpack8(q0, x0);
+  unpack8(q1, x1);
+  unpack8(q2, x2);
+  unpack8(q3, x3);
   const float pw[4] = {pg.x, pg.y, pg.z, pg.w};
-  const float4 cr[4] = {c0, c1, c2, c3};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float o[8];
@@ -495,7 +646,7 @@ __global__ __launch_bounds__(256) void mhc_post_kernel(const uint4* __restrict__
       a = __builtin_fmaf(cr[i].w, x3[e], a);
       o[e] = a;
     }
-    out[xb + (size_t)i * C8] = pack8(o);
+    nt_store16(pack8(o), out + xb + (size_t)i * C8);
   }
 }
 

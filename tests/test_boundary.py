@@ -38,9 +38,12 @@ def test_sizes():
     assert m.mhc_fn_packed_bytes(4 * C) == 4 * C * 24 * 4
     assert m.mhc_fn_packed_bytes(0) == 0
     assert m.mhc_workspace_bytes(1, 4, C) > 0
-    # large token counts use whole tiles per workgroup: the bound does not grow with T
-    assert m.mhc_workspace_bytes(1 << 20, 4, C) == m.mhc_workspace_bytes(4096, 4, C)
-    assert m.mhc_workspace_bytes(1 << 20, 4, C) < 2 * MiB
+    # few tokens: split partials, bounded; many tokens (grouped delayed form):
+    # 4 x 64 x 26 floats of partial sums per 64-token tile, ~416 B per token
+    assert m.mhc_workspace_bytes(1024, 4, C) < 2 * MiB
+    assert m.mhc_workspace_bytes(16384, 4, C) < 16384 * 512
+    assert m.mhc_workspace_bytes(1 << 20, 4, C) < (1 << 20) * 512
+    assert m.mhc_workspace_bytes(1 << 20, 4, 4096) < 2 * MiB   # no grouped form for C != 5120
     assert m.mhc_workspace_bytes(16, 3, C) == 0
     assert m.mhc_workspace_bytes(16, 4, 5000) == 0
     for s in range(8):
@@ -135,10 +138,13 @@ def test_entry_specific():
     assert call_entry(x=h, xo=h + 32) == ALIAS
 
 
-def test_large_tokens_need_no_workspace():
-    # T >= 4096: one workgroup per 16-token tile, nothing to combine.  Validation
-    # passes with no workspace; the launch then fails only for lack of a GPU.
-    assert call_delayed(T=4096, ws=None) == HIP
+def test_workspace_needs_by_form():
+    # T >= 2048, delayed, C = 5120: grouped form, partial sums go through the workspace
+    assert call_delayed(T=4096, ws=None) == WS
+    assert call_delayed(T=4096, ws_bytes=m.mhc_workspace_bytes(4096, 4, C) - 16) == WS
+    assert call_delayed(T=4096, ws_bytes=m.mhc_workspace_bytes(4096, 4, C)) == HIP
+    # own pre-mix at T >= 2048: one workgroup per 16-token tile, nothing to combine
+    assert call_pre(T=4096, ws=None) == HIP
 
 
 def test_valid_call_reaches_the_runtime():
