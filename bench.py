@@ -53,6 +53,37 @@ def entry_bytes(T, C=C, norm=True):
     return T * (C * 2 + NS * C * 2 + C * 2 + 96) + C * 24 * 4 + 108 + (C * 2 if norm else 0)
 
 
+KERNEL_SOURCES = ("decode_mhc_pre_amd/csrc/mhc_kernels.hpp", "decode_mhc_pre_amd/csrc/mhc_device.hpp",
+                  "decode_mhc_pre_amd/csrc/mhc.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "seam_T16384_hbm_counters.md")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary, or None
+    when the kernels changed since the counters were taken (source hash differs)."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    src = [ln.split(":", 1)[1].strip() for ln in lines if ln.startswith("source_hash:")]
+    if not src or src[0] != kernel_source_hash():
+        return None
+    for ln in lines:
+        if ln.startswith("traffic_bytes " + kernel_key + ":"):
+            return int(ln.split(":", 1)[1].strip())
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,14 +169,15 @@ def main():
     post_avg = sum(post_ms) / len(post_ms)
     pb, qb = pre_bytes(T_SEAM), post_bytes(T_SEAM)
     kernels = {
-        "mhc_pre_group_kernel (delayed, norm)": dict(avg_us=pre_avg * 1e3, alg_bytes=pb,
-                                        gbs=pb / (pre_avg * 1e-3) / 1e9),
-        "mhc_post_kernel": dict(avg_us=post_avg * 1e3, alg_bytes=qb, gbs=qb / (post_avg * 1e-3) / 1e9),
+        "mhc_pre_group_kernel": dict(avg_us=pre_avg * 1e3, alg_bytes=pb, gbs=pb / (pre_avg * 1e-3) / 1e9,
+                                     traffic=measured_traffic("mhc_pre_group_kernel")),
+        "mhc_post_kernel": dict(avg_us=post_avg * 1e3, alg_bytes=qb, gbs=qb / (post_avg * 1e-3) / 1e9,
+                                traffic=measured_traffic("mhc_post_kernel")),
     }
     for v in kernels.values():
         v["frac"] = v["gbs"] / HBM_PEAK_GBS
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    traffic = None
+    traffic = kernels[dom]["traffic"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(kernels[dom]["gbs"], 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kernels[dom]["frac"], 4),
                 "traffic": traffic}
