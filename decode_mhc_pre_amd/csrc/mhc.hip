@@ -64,9 +64,7 @@ size_t plan_ws_bytes(const Plan& pl) {
   if (pl.nsplit <= 1) return 0;
   return counter_bytes(pl) + (size_t)pl.ntile * pl.nsplit * kTileT * kPartStride * sizeof(float);
 }
-unsigned group_grid(const Plan& pl) {
-  return (unsigned)(kXcds * kGR * ((pl.gtiles + kXcds - 1) / kXcds));
-}
+unsigned group_grid(const Plan& pl) { return (unsigned)(kGR * pl.gtiles); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -350,21 +350,21 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
 // Sinkhorn; member 0 writes the gates, every member writes its columns of
 // layer_input.
 //
-// Group barrier.  Blocks are dispatched to the XCDs round-robin (block b on
-// XCD b % 8) and in order within an XCD, so the members of a group -- blocks
-// 8(kGR*j + r) + xcd for r = 0..kGR-1 -- are consecutive in one XCD's order
-// and share its L2: when the last member is dispatched the others are already
-// resident, and the only group that can be partially resident on an XCD is
-// the newest one.  The wait is nevertheless bounded (kSpinMax sleeps, well
-// over a second), so it always ends.  Arrival and departure counters are
-// reset by the last member to leave, so the workspace is left as found.
+// Group barrier.  A group is kGR consecutive blocks.  Blocks are dealt to the
+// XCDs round-robin and dispatched in order within each XCD, so a group's members
+// are the k-th blocks of kGR different XCDs; every group whose index is at most
+// the smallest index any of those XCDs has reached is fully resident and
+// completes, which frees slots for the next ones -- no cycle of waits can form.
+// (Under a single in-order dispatch queue the members are simply consecutive.)
+// The wait is nevertheless bounded (kSpinMax sleeps, well over a second), so it
+// always ends.  Arrival and departure counters are reset by the last member to
+// leave, so the workspace is left as found.
 // All global traffic of the sweep uses buffer instructions on per-tile
 // descriptors: rows past the last token of a ragged tile read as zero and
 // their stores are dropped by the descriptor's range check.
 constexpr int kGroupThreads = 256;   // 4 waves, one per SIMD
 constexpr int kGR = 4;               // workgroups per tile
 constexpr int kGT = 64;              // tokens per tile (16 per wave)
-constexpr int kXcds = 8;
 constexpr int kSpinMax = 1 << 24;
 constexpr int kGPart = 26;           // exchanged per token: P[24], sum x^2, sum y^2
 
@@ -424,10 +424,11 @@ void mhc_pre_group_kernel(PreParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int i = lane & 15;
   const int g = lane >> 4;
-  const int xcd = blockIdx.x % kXcds;
-  const int q = blockIdx.x / kXcds;
-  const int mem = q % kGR;                      // member of the group
-  const int tile = (q / kGR) * kXcds + xcd;
+  // a group is kGR consecutive blocks; with blocks dealt to the XCDs round-robin,
+  // member r always lands on the XCDs with index = r (mod kGR), so each XCD's
+  // L2 only ever holds one quarter of the packed weight
+  const int mem = blockIdx.x % kGR;             // member of the group
+  const int tile = blockIdx.x / kGR;
   const int t0 = tile * kGT;
   if (t0 >= p.T) return;                        // the whole group agrees
   const int wt0 = t0 + wave * kTileT;           // this wave's first token
