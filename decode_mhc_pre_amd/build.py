@@ -15,9 +15,13 @@ DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("mhc_device.hpp", "mhc_kern
     [os.path.join(INCLUDE, "mhc.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed FP32 VALU forms are switched off for all device code.
+# Packed FP32 VALU forms are switched off for all device code.  The
+# persistent pre kernel's 40-step sweep must unroll completely (its register
+# queues are indexed by step), which exceeds LLVM's default size limit for
+# pragma-requested unrolling.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-pragma-unroll-threshold=1000000",
          "-Wno-pass-failed", "-I" + INCLUDE]
 
 

@@ -19,26 +19,22 @@ using namespace mhc;
 constexpr int kTargetProjGroups = 128;
 constexpr int kMinKBPerSplit = 8;  // two 32-k steps per wave at least
 constexpr int kMaxC = 16384;
-// The grouped delayed kernel keeps a tile's collapsed rows on chip and splits
-// each 64-token tile over a group of workgroups: worth it once the groups fill
-// the chip.
+// The persistent delayed kernel keeps a tile's collapsed rows on chip and
+// splits each 64-token tile over a group of 16 workgroups: worth it once the
+// groups fill the chip.
 constexpr int kGroupC = 5120;
 constexpr int kGroupMinT = 2048;
-constexpr int kGroupYL = 16;  // collapsed-row blocks per wave kept in LDS
-constexpr int kGroupD = 4;    // prefetch distance in 32-column blocks
 
 struct Plan {
   int ntile, nsplit, nproj;
-  bool group;
-  int gtiles;  // grouped form: 64-token tiles
+  bool persist;  // persistent delayed form (C = 5120, many tokens)
 };
 
-Plan make_plan(int T, int KB, bool group_ok) {
+Plan make_plan(int T, int KB, bool persist_ok) {
   Plan pl;
   pl.ntile = (T + kTileT - 1) / kTileT;
-  pl.group = group_ok && T >= kGroupMinT;
-  pl.gtiles = (T + kGT - 1) / kGT;
-  int ns = (pl.group || pl.ntile >= kTargetProjGroups)
+  pl.persist = persist_ok && T >= kGroupMinT;
+  int ns = (pl.persist || pl.ntile >= kTargetProjGroups)
                ? 1
                : (kTargetProjGroups + pl.ntile - 1) / pl.ntile;
   int maxs = KB / kMinKBPerSplit;
@@ -51,20 +47,35 @@ Plan make_plan(int T, int KB, bool group_ok) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace layout: [counters, padded to 256 B][partial sums].
-//   split form:   counters [ntile] u32,      partials [ntile][nsplit][16][25] f32
-//   grouped form: counters [gtiles][2] u32,  partials [gtiles][kGR][64][26] f32
-size_t counter_bytes(const Plan& pl) {
-  const size_t n = pl.group ? 2 * (size_t)pl.gtiles : (size_t)pl.ntile;
-  return align_up(n * sizeof(unsigned), 256);
-}
+// Workspace layout.
+//   split form:      counters [ntile] u32 (padded to 256 B), partials [ntile][nsplit][16][25] f32
+//   persistent form: word 0 finished waves, word 2 wait-budget flag, arrival counters
+//                    [group][wave][3] 256 B apart from word 64; records [group][wave][2]
+//                    (1 KB sum-y^2 block + 32 KB value block) from 64 KiB
+size_t counter_bytes(const Plan& pl) { return align_up((size_t)pl.ntile * sizeof(unsigned), 256); }
 size_t plan_ws_bytes(const Plan& pl) {
-  if (pl.group)
-    return counter_bytes(pl) + (size_t)pl.gtiles * kGR * kGT * kGPart * sizeof(float);
+  if (pl.persist) return persist_ws_bytes();
   if (pl.nsplit <= 1) return 0;
   return counter_bytes(pl) + (size_t)pl.ntile * pl.nsplit * kTileT * kPartStride * sizeof(float);
 }
-unsigned group_grid(const Plan& pl) { return (unsigned)(kGR * pl.gtiles); }
+
+// Groups of the persistent kernel: one workgroup per CU at most (its LDS use
+// guarantees that), never more groups than tiles.
+int persist_groups(int T) {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  const int tiles = (T + kPT - 1) / kPT;
+  int ng = cus[dev] / kPG;
+  if (ng > kPMaxGroups) ng = kPMaxGroups;
+  if (ng > tiles) ng = tiles;
+  return ng;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -143,7 +154,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   if (any_alias(outs, 6, ins, 6)) return MHC_ERR_ALIAS;
 
   if (T == 0) return MHC_OK;
-  const Plan pl = make_plan(T, KB, mode == kModeDelayed && C == kGroupC);
+  Plan pl = make_plan(T, KB, mode == kModeDelayed && C == kGroupC);
   const size_t need = plan_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return MHC_ERR_WORKSPACE;
 
@@ -160,7 +171,9 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   p.li = li;
   p.xout = x_out;
   p.cnt = need ? static_cast<unsigned*>(ws) : nullptr;
-  p.part = need ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(pl)) : nullptr;
+  p.part = need ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                           (pl.persist ? kPPartOffset : counter_bytes(pl)))
+                : nullptr;
   p.eps = eps;
   p.iters = iters;
   p.T = T;
@@ -173,10 +186,20 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 block(kThreads);
-  if (pl.group) {
-    hipLaunchKernelGGL((mhc_pre_group_kernel<kGroupC, kGroupYL, kGroupD>), dim3(group_grid(pl)),
-                       dim3(kGroupThreads), 0, s, p);
-    return launched();
+  if (pl.persist) {
+    const int ng = persist_groups(T);
+    if (ng > 0) {
+      hipLaunchKernelGGL(mhc_pre_persist_kernel<kGroupC>, dim3(ng * kPG), block, 0, s, p, ng);
+      return launched();
+    }
+    // a device too small for one group: the split form (its workspace need is covered)
+    pl = make_plan(T, KB, false);
+    p.ntile = pl.ntile;
+    p.nsplit = pl.nsplit;
+    p.nproj = pl.nproj;
+    if (pl.nsplit > 1) {
+      p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(pl));
+    }
   }
   switch (mode) {
     case kModePre:
@@ -227,11 +250,8 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
       if (b > best) best = b;
     }
   }
-  // the grouped delayed form grows with the token count
-  if (C == kGroupC) {
-    const Plan pl = make_plan(T_max, MHC_HC_MULT * C / kKB, true);
-    if (pl.group && plan_ws_bytes(pl) > best) best = plan_ws_bytes(pl);
-  }
+  // the persistent delayed form: fixed size
+  if (C == kGroupC && T_max >= kGroupMinT && persist_ws_bytes() > best) best = persist_ws_bytes();
   return best;
 }
 

@@ -5,10 +5,11 @@
 //                               workgroups (few tokens) or one workgroup per
 //                               16-token tile, last-arriver reduction, gates +
 //                               Sinkhorn, collapse + folded RMSNorm.
-//   mhc_pre_group_kernel        delayed pre stage for many tokens (C = 5120):
-//                               one sweep over x; a 64-token tile split over a
-//                               group of workgroups on one XCD; projection, both
-//                               sums of squares, collapse and norm fused.
+//   mhc_pre_persist_kernel      delayed pre stage for many tokens (C = 5120):
+//                               persistent groups of 16 workgroups, one sweep
+//                               over x per 64-token tile; projection (weight
+//                               slice resident in LDS), both sums of squares,
+//                               collapse and norm fused.
 //   mhc_post_kernel             post stage: post_i * y + sum_j comb_ij x_j.
 #pragma once
 
@@ -327,280 +328,523 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
                                              s_pre[k][3], &s_tmp[0]);
 }
 
-// ------------------------------------------------------------------ pre kernel, grouped delayed form
-// Many tokens, hidden size fixed at compile time.  A tile of 64 tokens is
-// covered by a group of kGR workgroups; member r owns hidden columns
-// [r*C/kGR, (r+1)*C/kGR) of all four streams, and its wave w owns tokens
-// 16w..16w+15 of the tile.  The four waves walk the same 32-column blocks in
-// step, so each weight fragment is fetched from L2 once per workgroup and
-// served to the other waves from L1: the weight costs 1/64 of its size per
-// token instead of 1/16.  Per block a lane loads 8 bf16 of each stream for
-// one token (the MFMA A operand), so one sweep over x feeds, without
-// re-reading:
-//   - the partial projection (3 MFMAs per stream against the packed weight),
-//   - the partial row sum of squares (MFMA of the fragment with itself: its
-//     diagonal is the per-token sum),
-//   - the exact-order collapse with the carried pre-mix,
-//   - the partial sum of squares of the collapsed row (folded RMSNorm).
-// The collapsed rows stay on chip until the norm factor is known: most blocks
-// in registers, kYL blocks per wave in LDS; the registers this frees hold a
-// rotating prefetch kD blocks deep.  The members then exchange their partial
-// sums through the workspace (group barrier, below), every member reduces them
-// in member order -- the same bits in every member -- and runs gates +
-// Sinkhorn; member 0 writes the gates, every member writes its columns of
-// layer_input.
+// ------------------------------------------------------------------ pre kernel, persistent delayed form
+// Many tokens, hidden size fixed at compile time.  Tokens are cut into tiles
+// of 64; a group of kPG workgroups covers one tile at a time, member r owning
+// hidden columns [r*C/kPG, (r+1)*C/kPG) of all four streams, wave w owning
+// tokens 16w..16w+15.  The grid is persistent: group j walks tiles j,
+// j + ngroups, ...; a member's column range never changes, so its slice of
+// the packed projection weight (40 k-blocks, 120 KB) is copied into LDS once
+// and every MFMA B operand afterwards comes from LDS.
 //
-// Group barrier.  A group is kGR consecutive blocks.  Blocks are dealt to the
-// XCDs round-robin and dispatched in order within each XCD, so a group's members
-// are the k-th blocks of kGR different XCDs; every group whose index is at most
-// the smallest index any of those XCDs has reached is fully resident and
-// completes, which frees slots for the next ones -- no cycle of waits can form.
-// (Under a single in-order dispatch queue the members are simply consecutive.)
-// The wait is nevertheless bounded (kSpinMax sleeps, well over a second), so it
-// always ends.  Arrival and departure counters are reset by the last member to
-// leave, so the workspace is left as found.
-// All global traffic of the sweep uses buffer instructions on per-tile
+// Per tile a wave issues 40 loads of 16 B per lane (the MFMA A operand: 16
+// tokens x 8 columns), ordered so that two consecutive loads cover one full
+// 128-byte line of each token row, and keeps kPQ of them in flight; the queue
+// runs on into the next tile without a break.  Each load feeds, without being
+// re-read:
+//   - the partial projection (3 MFMAs against the LDS weight fragments),
+//   - the partial row sum of squares (MFMA of the fragment with itself: its
+//     diagonal holds the per-token sums),
+//   - one step of the exact-order collapse with the carried pre-mix
+//     (y = fl(fl(fl(fl(p0 x0) + fl(p1 x1)) + fl(p2 x2)) + fl(p3 x3)), each
+//     load adding one stream's product),
+//   - after the last stream of a column block, the partial sum of squares of
+//     the collapsed row (folded RMSNorm).
+// The collapsed rows of a tile stay in registers until the norm factor is
+// known: two buffers, one filling while the previous tile's waits for the
+// rest of its group.
+//
+// Exchange.  Each wave is in a group of 16 waves, the ones with its index in
+// the 16 members, sharing the same 16 tokens.  Its record per tile holds a
+// 1 KB block of row sums of squares of the collapsed rows, [member][token],
+// and a 32 KB block of the other 25 partial sums, [token][member][32] (24
+// projections and the row sum of squares of x, padded to a 128-byte line),
+// so that every store and load of the exchange moves whole lines: a member
+// writes 64 bytes and 2 KB, a reader loads 1 KB and its gate token's 2 KB.
+// At the end of tile k a wave stores its partial sums into record slot k & 1
+// and goes on without waiting.  The rest runs inside the next sweep, at fixed
+// steps, so that the x queue never drains:
+//   step kPQ:     increment slot k's arrival counter, once the first x load
+//                 issued after those stores has returned (vector memory
+//                 operations of a wave complete in issue order, so the stores
+//                 are complete as well);
+//   step 16:      read the counter; step 24: check it (only a member lagging
+//                 behind makes the wave wait) and load the group's records;
+//   step 32:      norm factors of the 16 tokens (every member sums the members'
+//                 partials in the same fixed order, so all hold the same bits)
+//                 and, over steps 32-39, the wave's columns of layer_input of
+//                 tile k from the parked buffer;
+//   step 32 on:   gates and Sinkhorn of one token (member r takes token r), one
+//                 iteration per step, written 21 steps later.
+// Slot k & 1 is rewritten at the end of tile k + 2, by which time every member
+// has consumed it: the writer checked at step 24 of tile k + 2 that every
+// member arrived for tile k + 1, which each does at step kPQ of tile k + 2,
+// after consuming tile k's records in tile k + 1.
+// Counters only grow within a call (target = kPG x uses of the slot); the
+// last wave of the grid to finish sets them back to zero, so the workspace is
+// left as found.
+//
+// Forward progress: a group is kPG consecutive blocks and blocks are dispatched
+// in order, so groups become resident whole or are preceded by groups that
+// are; those finish all their tiles and free their CUs.  The waits are bounded
+// nevertheless: a wave sleeps at most kSpinBudget times over the whole call
+// (a correct call needs a few at most); if the budget runs out it records the
+// fact in workspace word 2 and stops waiting, so the kernel always ends.
+// All x, pre_in and layer_input traffic uses buffer instructions on per-tile
 // descriptors: rows past the last token of a ragged tile read as zero and
-// their stores are dropped by the descriptor's range check.
-constexpr int kGroupThreads = 256;   // 4 waves, one per SIMD
-constexpr int kGR = 4;               // workgroups per tile
-constexpr int kGT = 64;              // tokens per tile (16 per wave)
-constexpr int kSpinMax = 1 << 24;
-constexpr int kGPart = 26;           // exchanged per token: P[24], sum x^2, sum y^2
+// their stores are dropped by the range check; a descriptor of zero bytes
+// stands for "no such tile", so the first and last tiles need no branches.
+constexpr int kPG = 16;          // members (workgroups) per tile group
+constexpr int kPT = 64;          // tokens per tile, 16 per wave
+constexpr int kPQ = 8;           // x loads in flight per wave
+constexpr int kPMaxGroups = 16;  // at most 256 workgroups; the workspace is sized for this many groups
+constexpr int kPVals = 25;       // exchanged per token besides sum y^2: P[24], sum x^2
+constexpr int kPLine = 32;       // floats per (token, member) in the value block: one 128-byte line
+constexpr int kPSsy = kPG * kTileT;                    // floats of the sum-y^2 block
+constexpr int kPRec = kPSsy + kTileT * kPG * kPLine;   // floats per (group, wave, slot)
+constexpr int kPRing = 2;        // record slots per (group, wave)
+// Workspace: word 0 counts finished waves, word 2 flags a wait that ran out of
+// budget; arrival counters from word kPCntBase, one per (group, wave, slot)
+// plus a scratch one (slot kPRing) for the first tile, each alone in its own
+// 256-byte block (packed together, the chip's polls would all land on one
+// memory channel); records from byte kPPartOffset.
+constexpr int kPCntBase = 64;
+constexpr int kPCntStride = 64;  // words
+constexpr int kPSlots = kPRing + 1;
+constexpr size_t kPPartOffset = 64 * 1024;
+constexpr int kSpinBudget = 1 << 20;  // sleeps per wave over the whole call (about a second)
+// steps of a tile at which the exchange of the previous tile advances
+constexpr int kPArrive = kPQ;    // arrive for the previous tile
+constexpr int kPCnt = 16;        // read its counter
+constexpr int kPCheck = 24;      // check it, load the records
+constexpr int kPUse = 32;        // norm factors, layer_input, Sinkhorn start
+constexpr int kPGateEnd = 13;    // step of the following tile at which the gates are written
 
-// Partial sums cross workgroups (possibly XCDs) through device-coherent
-// accesses: agent-scope atomic stores and loads, each coherent on its own, so
-// no release fence has to write back the L2 (measured: such a fence cost ~20 us
-// per workgroup here, flushing other workgroups' dirty layer_input lines).  A
-// writer waits for its own stores to complete before the workgroup barrier
-// that precedes the arrival increment.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+inline size_t persist_ws_bytes() {
+  return kPPartOffset + (size_t)kPMaxGroups * kNS * kPRing * kPRec * sizeof(float);
 }
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// Partial sums cross workgroups (and XCDs) through device-coherent accesses:
+// agent-scope atomic stores and loads, each coherent on its own, so no release
+// fence has to write back the L2.
+__device__ __forceinline__ void buf_store16_agent(uint4 v, rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 16);
 }
 __device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void wait_stores() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// LDS-only barrier: waits for this wave's LDS traffic, then s_barrier.  Unlike
-// __syncthreads it does not wait for outstanding global loads, so the
-// prefetched blocks stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+__device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+constexpr int kWaitVmem0 = 0x0f70;   // s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained (gfx9 encoding)
+constexpr int kAuxAgent = 16;    // buffer cache policy: coherent at device scope (sc1)
+__device__ __forceinline__ uint4 buf_load16_agent(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAuxAgent));
+}
+// An opaque zero that the compiler cannot compute before `v` is in a register:
+// whatever uses it waits for the load that produced `v`.
+__device__ __forceinline__ unsigned zero_after(unsigned v) {
+  unsigned z;
+  __asm__ volatile("v_and_b32 %0, 0, %1" : "=v"(z) : "v"(v));
+  return z;
 }
 
-template <int kC, int kYL, int kD>
-__global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mhc_pre_group_kernel(PreParams p) {
-  constexpr int kNW = kGroupThreads / kWave;
-  constexpr int kKBC = kC / kKB;          // 32-column blocks per stream
-  constexpr int kCBW = kKBC / kGR;        // blocks per member (all waves walk the same ones)
-  constexpr int kRow = kNS * kC * 2;      // bytes of one token's residual row
-  constexpr int kSlots = kD + 1;
-  constexpr int kFrag = kFragPerKB * kWave * 16;  // bytes of one k-block of packed weight
-  static_assert(kKBC % kGR == 0, "hidden size must split evenly over the group");
-  static_assert(kNW * kTileT == kGT, "one 16-token MFMA tile per wave");
-  static_assert(kNW == kNS, "wave w fetches the weight fragments of stream w");
-  static_assert(kYL <= kCBW, "more LDS blocks than blocks");
-  __shared__ float4 s_y[kNW][kYL > 0 ? kYL : 1][2][kWave];  // collapsed rows kept in LDS
-  __shared__ float s_pre[kGT][kNS];
-  __shared__ float s_ry[kGT];
-  __shared__ uint4 s_w[kCBW][4];    // this member's columns of the norm weight (bf16)
-  // the weight block ring (2 x 12 KB) is only live during the sweep; afterwards
-  // the same bytes hold the per-wave partial sums and the reduced tile sums
-  typedef uint4 FnRing[2][kNS][kFragPerKB][kWave];
-  typedef float RedBuf[kNW][kTileT][52];
-  typedef float TileBuf[kGT][kPS];
-  static_assert(sizeof(RedBuf) + sizeof(TileBuf) <= sizeof(FnRing), "reuse of the ring");
-  __shared__ FnRing s_fn;
-  RedBuf& s_red = *reinterpret_cast<RedBuf*>(&s_fn[0][0][0][0]);
-  TileBuf& s_P = *reinterpret_cast<TileBuf*>(reinterpret_cast<char*>(&s_fn[0][0][0][0]) + sizeof(RedBuf));
+// Gates and Sinkhorn of one token, in pieces.  The token's 25 summed values
+// (P[24], sum x^2) sit in `v`; `ba` holds bias[24] then alpha[3] (both LDS:
+// no global load here, whose wait would also wait for every x load in
+// flight).  Every quad of the wave computes the same token (lane & 3 = comb
+// row); quad 0 writes.  Same arithmetic as tile_gates.
+struct TokenGates {
+  float m[4];
+  float pr, po;
+  int tok, it;
+  bool write;
+
+  __device__ __forceinline__ void init(const PreParams& p, const float* v, const float* ba, int t,
+                                       bool w) {
+    const int row = threadIdx.x & 3;
+    const float r = 1.0f / sqrtf(v[24] / (float)p.K + p.eps);
+    const float ac = ba[kNL + 2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = ac * (r * v[8 + 4 * row + j]) + ba[8 + 4 * row + j];
+    const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = expf(m[j] - mx);
+    const float lp = ba[kNL] * (r * v[row]) + ba[row];
+    const float lq = ba[kNL + 1] * (r * v[4 + row]) + ba[4 + row];
+    pr = 1.0f / (1.0f + expf(-lp));
+    po = 2.0f / (1.0f + expf(-lq));
+    tok = t;
+    it = 0;
+    write = w;
+  }
+  __device__ __forceinline__ void step(int iters) {   // one Sinkhorn iteration, if any are left
+    if (it < iters) {
+      const float inv = __builtin_amdgcn_rcpf((m[0] + m[1]) + (m[2] + m[3]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m[j] *= inv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float c = m[j] + dpp_quad_xor1(m[j]);
+        c = c + dpp_quad_xor2(c);
+        m[j] *= __builtin_amdgcn_rcpf(c);
+      }
+      ++it;
+    }
+  }
+  __device__ __forceinline__ void finish(const PreParams& p) {
+    while (it < p.iters) step(p.iters);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int row = lane & 3;
+    if (write && lane < 4 && tok < p.T) {
+      reinterpret_cast<float4*>(p.comb)[(size_t)tok * 4 + row] = make_float4(m[0], m[1], m[2], m[3]);
+      p.pre[(size_t)tok * kNS + row] = pr;
+      p.post[(size_t)tok * kNS + row] = po;
+    }
+    write = false;
+  }
+};
+
+template <int kC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mhc_pre_persist_kernel(PreParams p, int ngroups) {
+  constexpr int kCBM = kC / kKB / kPG;   // 32-column blocks per member and stream
+  constexpr int kLd = kNS * kCBM;        // x loads per wave and tile
+  constexpr int kRow = kNS * kC * 2;     // bytes of one token's residual row
+  constexpr int kUnit = 2 * kNS;         // loads covering two column blocks of all streams
+  constexpr int kFragRows = kLd * kFragPerKB;
+  constexpr int kNW = kThreads / kWave;
+  static_assert(kC % (kKB * kPG) == 0 && kCBM % 2 == 0, "hidden size must split into column-block pairs");
+  static_assert(kLd == 40 && kLd % kPQ == 0, "the exchange schedule assumes 40 loads per tile");
+  static_assert(kNW * kTileT == kPT, "one 16-token MFMA tile per wave");
+  __shared__ uint4 s_fnv[kLd * kFragPerKB * kWave];  // this member's weight: [stream*kCBM + block][frag][lane]
+  __shared__ uint4 s_w[kCBM][4];                    // this member's columns of the norm weight
+  __shared__ float s_red[kNW][kTileT][52];          // per wave: MFMA D layout -> token rows
+  __shared__ float4 s_xs[kNW][kPSsy / 4];             // per wave: loaded sum-y^2 block
+  __shared__ float4 s_xv[kNW][kPG * kPLine / 4];     // per wave: loaded value block of its gate token
+  __shared__ float s_gv[kNW][32];                   // per wave: the summed values of its gate token
+  __shared__ float s_ba[32];                        // bias[24], alpha[3]
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int i = lane & 15;
   const int g = lane >> 4;
-  // a group is kGR consecutive blocks; with blocks dealt to the XCDs round-robin,
-  // member r always lands on the XCDs with index = r (mod kGR), so each XCD's
-  // L2 only ever holds one quarter of the packed weight
-  const int mem = blockIdx.x % kGR;             // member of the group
-  const int tile = blockIdx.x / kGR;
-  const int t0 = tile * kGT;
-  if (t0 >= p.T) return;                        // the whole group agrees
-  const int wt0 = t0 + wave * kTileT;           // this wave's first token
-  // descriptors depend on the block only (they must stay in SGPRs); a lane's
-  // token row within the tile goes into its offset, which the range check covers
-  const int nvalid = min(kGT, p.T - t0);
-  const int tw = wave * kTileT + i;             // the lane's token within the tile
-  const rsrc_t rx = make_rsrc(p.x + (size_t)t0 * (kNS * kC), nvalid * kRow);
-  const rsrc_t rf = make_rsrc(p.fnp, p.KB * kFrag);
-  const rsrc_t rp = make_rsrc(p.pre_in + (size_t)t0 * kNS, nvalid * 16);
-  const int xlane = tw * kRow + g * 16;
-  const int flane = lane * 16;
-  const uint4 pv = buf_load16(rp, tw * 16, 0);
-  const float p0 = __uint_as_float(pv.x), p1 = __uint_as_float(pv.y);
-  const float p2 = __uint_as_float(pv.z), p3 = __uint_as_float(pv.w);
-  const int cb0 = mem * kCBW;                   // first column block of this member
-  if (p.nw && tid < kCBW * 4)
-    s_w[tid >> 2][tid & 3] = reinterpret_cast<const uint4*>(p.nw)[cb0 * 4 + tid];
-  // tiles walk their blocks from different starting points, so that at any
-  // time the chip's x reads spread over many columns (and L2 channels)
-  const int rot = (tile * 7) % kCBW;
-
-  // rotating prefetch: slot k holds block b with b % kSlots == k; per block a
-  // wave fetches its tokens' x (4 streams) and one stream's weight fragments
-  uint4 xq[kSlots][kNS];
-  uint4 fq[kSlots][kFragPerKB];
-  auto issue = [&](int cb, int slot) {
-    int blk = cb + rot;
-    blk = blk >= kCBW ? blk - kCBW : blk;
-    const int cbg = cb0 + blk;
-#pragma unroll
-    for (int s = 0; s < kNS; ++s) xq[slot][s] = buf_load16(rx, xlane, (s * kC + cbg * kKB) * 2);
-#pragma unroll
-    for (int f = 0; f < kFragPerKB; ++f)
-      fq[slot][f] = buf_load16(rf, flane, (wave * kKBC + cbg) * kFrag + f * kWave * 16);
-  };
-#pragma unroll
-  for (int d = 0; d < kD; ++d) issue(d, d);
-
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, as = a0;
-  float ssy = 0.f;
-  float y[kCBW - kYL][8];
-#pragma unroll
-  for (int cb = 0; cb < kCBW; ++cb) {
-    if (cb + kD < kCBW) issue(cb + kD, (cb + kD) % kSlots);
-    const int slot = cb % kSlots;
-    // publish this wave's stream of the weight block, then read all four
-#pragma unroll
-    for (int f = 0; f < kFragPerKB; ++f) s_fn[cb & 1][wave][f][lane] = fq[slot][f];
-    lds_barrier();
-#pragma unroll
-    for (int s = 0; s < kNS; ++s) {
-      a0 = mfma_bf16(xq[slot][s], s_fn[cb & 1][s][0][lane], a0);
-      a1 = mfma_bf16(xq[slot][s], s_fn[cb & 1][s][1][lane], a1);
-      a2 = mfma_bf16(xq[slot][s], s_fn[cb & 1][s][2][lane], a2);
-      as = mfma_bf16(xq[slot][s], xq[slot][s], as);
-    }
-    float yb[8];
-    collapse8(xq[slot][0], xq[slot][1], xq[slot][2], xq[slot][3], p0, p1, p2, p3, yb);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(yb[e], yb[e], ssy);
-    if (cb < kYL) {
-      s_y[wave][cb][0][lane] = make_float4(yb[0], yb[1], yb[2], yb[3]);
-      s_y[wave][cb][1][lane] = make_float4(yb[4], yb[5], yb[6], yb[7]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[cb - kYL][e] = yb[e];
-    }
-  }
-
-  // diagonal of x.x^T: row 4g + r of lane (g, i) is token i when i == 4g + r
-  float ssx = 0.f;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if (i == 4 * g + r) ssx = as[r];
-  ssy += __shfl_xor(ssy, 16);
-  ssy += __shfl_xor(ssy, 32);
-  __syncthreads();  // every wave is done with the weight ring
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    s_red[wave][4 * g + r][i] = a0[r];
-    s_red[wave][4 * g + r][16 + i] = a1[r];
-    s_red[wave][4 * g + r][32 + i] = a2[r];
-  }
-  if ((i >> 2) == g) s_red[wave][i][48] = ssx;
-  if (g == 0) s_red[wave][i][49] = ssy;
-  __syncthreads();
-
-  // ---- publish this member's partials: token (wave, tt), values 6*part .. 6*part+5
-  float* part = p.part + (size_t)tile * kGR * kGT * kGPart;
-  {
-    const int tt = lane >> 2, pp = lane & 3;
-    float* dst = part + ((size_t)mem * kGT + wave * kTileT + tt) * kGPart;
-#pragma unroll
-    for (int u = 0; u < 6; ++u) {
-      const int j = pp * 6 + u;
-      st_agent(dst + j, s_red[wave][tt][j] + s_red[wave][tt][kNL + j]);
-    }
-    if (pp < 2) st_agent(dst + kNL + pp, s_red[wave][tt][48 + pp]);
-  }
-  wait_stores();
-  __syncthreads();
-  unsigned* arrive = p.cnt + 2 * tile;
-  unsigned* depart = arrive + 1;
-  if (tid == 0) {
-    __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int spins = 0;
-    while (ld_agent(arrive) < (unsigned)kGR && spins < kSpinMax) {
-      __builtin_amdgcn_s_sleep(2);
-      ++spins;
-    }
-  }
-  __syncthreads();
-  {
-    // sum the members' partials in member order: token tid >> 2, values of part tid & 3
-    const int tt = tid >> 2, pp = tid & 3;
-    const int nj = pp < 2 ? 7 : 6;  // parts 0/1 also carry sum x^2 / sum y^2
-#pragma unroll
-    for (int u = 0; u < 7; ++u) {
-      if (u < nj) {
-        const int j = u < 6 ? pp * 6 + u : kNL + pp;
-        float acc = 0.f;
-#pragma unroll
-        for (int m = 0; m < kGR; ++m)
-          acc += ld_agent(part + ((size_t)m * kGT + tt) * kGPart + j);
-        s_P[tt][j] = acc;
-      }
-    }
-  }
-  __syncthreads();
-  if (tid == 0 && atomicAdd(depart, 1u) == (unsigned)(kGR - 1)) {
-    atomicExch(arrive, 0u);  // every member has passed the barrier: reset for the next call
-    atomicExch(depart, 0u);
-  }
-
-  // ---- gates (member 0 writes them) and norm factor, each wave its 16 tokens
-  tile_gates(p, &s_P[wave * kTileT], wt0, &s_pre[wave * kTileT], mem == 0);
-  if (lane < kTileT) {
-    const int tt = wave * kTileT + lane;
-    s_ry[tt] = p.nw ? 1.0f / sqrtf(s_P[tt][25] / (float)kC + p.eps) : 1.0f;
-  }
-  __syncthreads();
-
-  const float ry = s_ry[tw];
-  const rsrc_t rl = make_rsrc(p.li + (size_t)t0 * kC, nvalid * kC * 2);
-  const int llane = tw * (kC * 2) + g * 16;
+  const int mem = blockIdx.x % kPG;
+  const int grp = blockIdx.x / kPG;
+  const int ntiles = (p.T + kPT - 1) / kPT;
+  const int nk = (ntiles - 1 - grp) / ngroups + 1;   // tiles of this group (launch: ngroups <= ntiles)
+  const int cb0 = mem * kCBM;
+  const int xlane = (wave * kTileT + i) * kRow + g * 16;
+  const int plane = (wave * kTileT + i) * 16;
+  const int llane = (wave * kTileT + i) * (kC * 2) + g * 16;
   const bool norm = p.nw != nullptr;
+
+  // descriptors of the group's k-th tile (k < 0 or k >= nk: zero bytes)
+  auto tile_of = [&](int k) { return (k >= 0 && k < nk) ? grp + k * ngroups : -1; };
+  auto tile_rows = [&](int t) { return t >= 0 ? min(kPT, p.T - t * kPT) : 0; };
+  auto x_rsrc = [&](int t) {
+    return make_rsrc(p.x + (size_t)max(t, 0) * kPT * (kNS * kC), tile_rows(t) * kRow);
+  };
+  auto pin_rsrc = [&](int t) { return make_rsrc(p.pre_in + (size_t)max(t, 0) * kPT * kNS, tile_rows(t) * 16); };
+  auto li_rsrc = [&](int t) { return make_rsrc(p.li + (size_t)max(t, 0) * kPT * kC, tile_rows(t) * kC * 2); };
+  const int xsoff = cb0 * kKB * 2;   // byte offset of this member's first column (SGPR)
+  int xls[kNS];                      // lane offset of each stream; the block offset fits the immediate
 #pragma unroll
-  for (int cb = 0; cb < kCBW; ++cb) {
-    int blk = cb + rot;
-    blk = blk >= kCBW ? blk - kCBW : blk;
-    const int c = (cb0 + blk) * kKB;
-    float yb[8];
-    if (cb < kYL) {
-      const float4 u = s_y[wave][cb][0][lane], v = s_y[wave][cb][1][lane];
-      yb[0] = u.x; yb[1] = u.y; yb[2] = u.z; yb[3] = u.w;
-      yb[4] = v.x; yb[5] = v.y; yb[6] = v.z; yb[7] = v.w;
-    } else {
+  for (int s = 0; s < kNS; ++s) xls[s] = xlane + s * kC * 2;
+  __asm__ volatile("" : "+v"(xls[0]), "+v"(xls[1]), "+v"(xls[2]), "+v"(xls[3]));
+  // load n of a tile: unit n / kUnit covers column blocks 2u, 2u + 1; within it
+  // stream-major, so loads 2q, 2q + 1 are the two halves of a 128-byte line
+  auto x_load = [&](rsrc_t r, int n) {
+    const int u = n / kUnit, q = n % kUnit;
+    const int s = q >> 1, cb = 2 * u + (q & 1);
+    return buf_load16(r, xls[s] + cb * kKB * 2, xsoff);
+  };
+
+  unsigned* cnt_base = p.cnt + kPCntBase + (grp * kNW + wave) * kPSlots * kPCntStride;
+  float* rec_base = p.part + (size_t)(grp * kNW + wave) * kPRing * kPRec;
+  // counter, arrival target and record of the group's k-th tile (k < 0: the scratch counter)
+  auto cnt_of = [&](int k) { return cnt_base + (k >= 0 ? (k & 1) : kPRing) * kPCntStride; };
+  auto target_of = [&](int k) { return k >= 0 ? (unsigned)kPG * (unsigned)((k >> 1) + 1) : 0u; };
+  auto rec_rsrc = [&](int k) {
+    return make_rsrc(rec_base + (size_t)(k >= 0 ? k & 1 : 0) * kPRec, k >= 0 ? kPRec * 4 : 0);
+  };
+
+  // ---- prologue: first x loads and pre_in, then the weight slice into LDS
+  rsrc_t rx = x_rsrc(tile_of(0));
+  uint4 xq[kPQ];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) yb[e] = y[cb - kYL][e];
+  for (int d = 0; d < kPQ; ++d) xq[d] = x_load(rx, d);
+  uint4 pq = buf_load16(pin_rsrc(tile_of(0)), plane, 0);
+  for (int r0 = 0; r0 < kFragRows; r0 += kNW * 10) {
+    uint4 v[10];
+#pragma unroll
+    for (int u = 0; u < 10; ++u) {
+      const int fr = r0 + wave + u * kNW;   // fragment row: (stream*kCBM + block)*3 + frag
+      const int lb = fr / kFragPerKB, f = fr - lb * kFragPerKB;
+      const int s = lb / kCBM, cb = lb - s * kCBM;
+      const int kbg = s * (kC / kKB) + cb0 + cb;
+      v[u] = fr < kFragRows ? p.fnp[((size_t)kbg * kFragPerKB + f) * kWave + lane] : make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int u = 0; u < 10; ++u) {
+      const int fr = r0 + wave + u * kNW;
+      if (fr < kFragRows) s_fnv[fr * kWave + lane] = v[u];
+    }
+  }
+  if (norm && tid < kCBM * 4) s_w[tid >> 2][tid & 3] = reinterpret_cast<const uint4*>(p.nw)[cb0 * 4 + tid];
+  if (tid < kNL) s_ba[tid] = p.bias[tid];
+  if (tid >= 32 && tid < 35) s_ba[kNL + tid - 32] = p.alpha[tid - 32];
+  __syncthreads();
+
+  float y0[kCBM][8], y1[kCBM][8];
+  uint4 pv[3];      // the previous tile's records, in flight: sum-y^2 block, gate token's values
+  unsigned cv = 0;  // the previous tile's arrival counter
+  TokenGates gt;
+  gt.m[0] = gt.m[1] = gt.m[2] = gt.m[3] = 1.0f;
+  gt.pr = gt.po = 0.0f;
+  gt.tok = -1;
+  gt.write = false;
+  gt.it = 0;
+
+  // weight fragments: two LDS base indices, each access within the 16-bit
+  // immediate offset of ds_read (the slice is 120 KB)
+  constexpr int kHalfLb = kLd / 2;
+  int fb0 = lane, fb1 = lane + kHalfLb * kFragPerKB * kWave;
+  __asm__ volatile("" : "+v"(fb0), "+v"(fb1));   // two bases: the compiler must not merge them
+  auto frag = [&](int lb, int f) -> uint4 {
+    return lb < kHalfLb ? s_fnv[fb0 + (lb * kFragPerKB + f) * kWave]
+                        : s_fnv[fb1 + ((lb - kHalfLb) * kFragPerKB + f) * kWave];
+  };
+  // the three weight fragments of load n's k-block, read one step ahead
+  uint4 fq[kFragPerKB];
+  auto fetch_frags = [&](int n) {
+    const int u = n / kUnit, q = n % kUnit;
+    const int lb = (q >> 1) * kCBM + 2 * u + (q & 1);
+#pragma unroll
+    for (int f = 0; f < kFragPerKB; ++f) fq[f] = frag(lb, f);
+  };
+  fetch_frags(0);
+
+  int budget = kSpinBudget;
+  auto wait_count = [&](const unsigned* c, unsigned target, unsigned v) {
+    while ((int)(v - target) < 0 && budget > 0) {
+      --budget;
+      __builtin_amdgcn_s_sleep(2);
+      v = ld_agent(c);
+    }
+    if ((int)(v - target) < 0 && lane == 0)
+      __hip_atomic_store(p.cnt + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every load of this wave is complete when the loop ends, so the straight
+    // path's wait counts stay valid after it
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+  };
+  // the group's records of tile kk: the 1 KB sum-y^2 block and the 2 KB of
+  // the gate token (member index), whole lines
+  auto load_records = [&](int kk) {
+    const rsrc_t rr = rec_rsrc(kk);
+    pv[0] = buf_load16_agent(rr, lane * 16, 0);
+    pv[1] = buf_load16_agent(rr, (kPSsy + mem * kPG * kPLine) * 4 + lane * 16, 0);
+    pv[2] = buf_load16_agent(rr, (kPSsy + mem * kPG * kPLine) * 4 + (kWave + lane) * 16, 0);
+  };
+  // norm factor of token i (returned) and the gate token's summed values (-> s_gv)
+  auto use_records = [&]() {
+    s_xs[wave][lane] = __builtin_bit_cast(float4, pv[0]);
+    s_xv[wave][lane] = __builtin_bit_cast(float4, pv[1]);
+    s_xv[wave][kWave + lane] = __builtin_bit_cast(float4, pv[2]);
+    const float* xs = reinterpret_cast<const float*>(s_xs[wave]);
+    const float* xv = reinterpret_cast<const float*>(s_xv[wave]);
+    // token i, members 4g..4g+3, then the four groups: the same order in every member
+    const float sg = ((xs[(4 * g) * kTileT + i] + xs[(4 * g + 1) * kTileT + i]) + xs[(4 * g + 2) * kTileT + i]) +
+                     xs[(4 * g + 3) * kTileT + i];
+    float sy = sg + __shfl_xor(sg, 16);
+    sy = sy + __shfl_xor(sy, 32);
+    if (lane < kPVals) {
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < kPG; ++m) acc += xv[m * kPLine + lane];
+      s_gv[wave][lane] = acc;
+    }
+    return norm ? 1.0f / sqrtf(sy / (float)kC + p.eps) : 1.0f;
+  };
+  auto li_store = [&](const float (&yb)[8], float ry, rsrc_t rl, int cb) {
     float o[8];
     if (norm) {
       float w[8];
-      unpack8(s_w[c / kKB - cb0][g], w);
+      unpack8(s_w[cb][g], w);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (yb[e] * ry) * w[e];
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = yb[e];
     }
-    buf_store16(pack8(o), rl, llane, c * 2);
+    buf_store16(pack8(o), rl, llane + cb * kKB * 2, xsoff);
+  };
+
+  // One tile: sweep of the group's k-th tile into ycur; exchange of tile k-1
+  // and its layer_input from yold.
+  auto tile_body = [&](int k, float (&ycur)[kCBM][8], float (&yold)[kCBM][8]) __attribute__((always_inline)) {
+#pragma clang fp contract(off)
+    // re-define the base offsets in every tile, so that base + constant is
+    // formed here (and folds into the instructions' offset fields) instead of
+    // being hoisted into one register per access
+    __asm__ volatile("" : "+v"(xls[0]), "+v"(xls[1]), "+v"(xls[2]), "+v"(xls[3]), "+v"(fb0), "+v"(fb1));
+    const int tnext = tile_of(k + 1);
+    const rsrc_t rxn = x_rsrc(tnext);
+    const float p0 = __uint_as_float(pq.x), p1 = __uint_as_float(pq.y);
+    const float p2 = __uint_as_float(pq.z), p3 = __uint_as_float(pq.w);
+    const int t1 = tile_of(k - 1);
+    const rsrc_t rl1 = li_rsrc(t1);
+    unsigned* cnt1 = cnt_of(k - 1);
+    const unsigned target1 = target_of(k - 1);
+    float ry1 = 1.0f;
+
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, as = a0;
+    float ssy = 0.f;
+#pragma unroll
+    for (int n = 0; n < kLd; ++n) {
+      const uint4 xv = xq[n % kPQ];
+      const int u = n / kUnit, q = n % kUnit;
+      const int s = q >> 1, cb = 2 * u + (q & 1);
+      a0 = mfma_bf16(xv, fq[0], a0);
+      a1 = mfma_bf16(xv, fq[1], a1);
+      a2 = mfma_bf16(xv, fq[2], a2);
+      as = mfma_bf16(xv, xv, as);
+      // the next step's weight fragments (the order of k-blocks is the same in every tile)
+      fetch_frags((n + 1) % kLd);
+      float f[8];
+      unpack8(xv, f);
+      const float ps = s == 0 ? p0 : s == 1 ? p1 : s == 2 ? p2 : p3;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ycur[cb][e] = s == 0 ? ps * f[e] : ycur[cb][e] + ps * f[e];
+      if (s == kNS - 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(ycur[cb][e], ycur[cb][e], ssy);
+      }
+      // refill: this tile's load n + kPQ, or the next tile's first loads
+      const int m = n + kPQ;
+      if (m < kLd) {
+        xq[n % kPQ] = x_load(rx, m);
+      } else {
+        xq[n % kPQ] = x_load(rxn, m - kLd);
+        if (m == kLd) pq = buf_load16(pin_rsrc(tnext), plane, 0);
+      }
+      // ---- exchange of tile k-1
+      if (n == kPArrive) {
+        // xv is the first x load issued after tile k-1's records were stored
+        const unsigned z = zero_after(xv.x);
+        if (lane == 0) __hip_atomic_fetch_add(cnt1, 1u + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (n == kPCnt) {
+        cv = ld_agent(cnt1);
+        __asm__ volatile("" ::: "memory");   // keep the read here, kPCheck - kPCnt steps ahead of its use
+      }
+      if (n == kPCheck) {
+        cv += zero_after(xv.y);              // the check cannot move above this step
+        if ((int)(cv - target1) < 0) wait_count(cnt1, target1, cv);
+        load_records(k - 1);
+        __asm__ volatile("" ::: "memory");   // issued here, used kPUse - kPCheck steps later
+      }
+      if (n == kPUse) {
+        ry1 = use_records();
+        gt.init(p, s_gv[wave], s_ba, t1 * kPT + wave * kTileT + mem, t1 >= 0);
+      }
+      if (n >= kPUse) {
+        // layer_input of tile k-1: ten column blocks over the last eight steps
+        const int c0 = n == kPUse ? 0 : n == kPUse + 1 ? 2 : n - kPUse + 2;
+        const int c1 = n == kPUse ? 2 : n == kPUse + 1 ? 4 : n - kPUse + 3;
+        for (int c = c0; c < c1 && c < kCBM; ++c) li_store(yold[c], ry1, rl1, c);
+        if (n > kPUse) gt.step(p.iters);
+      }
+      if (n < kPGateEnd) gt.step(p.iters);   // Sinkhorn of the previous gate token
+      if (n == kPGateEnd) gt.finish(p);
+      // keep every step's work in its step: the scheduler would otherwise sink
+      // the refill loads toward their use (shortening the queue) under the
+      // register pressure of the parked buffers
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    rx = rxn;
+
+    // ---- this tile's partial sums -> record slot k & 1 (no wait)
+    {
+      float ssx = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (i == 4 * g + r) ssx = as[r];
+      float t = ssy + __shfl_xor(ssy, 16);
+      t += __shfl_xor(t, 32);
+      float (*red)[52] = s_red[wave];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        red[4 * g + r][i] = a0[r];
+        red[4 * g + r][16 + i] = a1[r];
+        red[4 * g + r][32 + i] = a2[r];
+      }
+      if ((i >> 2) == g) red[i][48] = ssx;
+      if (g == 0) red[i][49] = t;
+      const rsrc_t rr = rec_rsrc(k);
+      // value block: this member's line of each token, 128 chunks of 16 B (chunk
+      // c: token c >> 3, values 4 (c & 7) .. +3; P = hi + lo, then sum x^2, zeros)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = h * kWave + lane;
+        const int tt = c >> 3, v0 = 4 * (c & 7);
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = v0 + e;
+          o[e] = j < kNL ? red[tt][j] + red[tt][kNL + j] : j == kNL ? red[tt][48] : 0.f;
+        }
+        buf_store16_agent(make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                                     __float_as_uint(o[3])),
+                          rr, (kPSsy + (tt * kPG + mem) * kPLine + v0) * 4, 0);
+      }
+      // sum-y^2 block: this member's 16 tokens, 64 bytes
+      if (lane < 4)
+        buf_store16_agent(make_uint4(__float_as_uint(red[4 * lane][49]), __float_as_uint(red[4 * lane + 1][49]),
+                                     __float_as_uint(red[4 * lane + 2][49]), __float_as_uint(red[4 * lane + 3][49])),
+                          rr, (mem * kTileT + 4 * lane) * 4, 0);
+    }
+  };
+
+  // After the last tile kl: its exchange and layer_input (buffer ylast),
+  // waiting as needed.
+  auto tail = [&](int kl, float (&ylast)[kCBM][8]) __attribute__((always_inline)) {
+    gt.finish(p);
+    wait_vmem();   // tile kl's records are stored
+    unsigned* c = cnt_of(kl);
+    if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned v = ld_agent(c);
+    if ((int)(v - target_of(kl)) < 0) wait_count(c, target_of(kl), v);
+    load_records(kl);
+    const float ry = use_records();
+    const int t = tile_of(kl);
+    gt.init(p, s_gv[wave], s_ba, t * kPT + wave * kTileT + mem, true);
+    const rsrc_t rl = li_rsrc(t);
+#pragma unroll
+    for (int cb = 0; cb < kCBM; ++cb) li_store(ylast[cb], ry, rl, cb);
+    gt.finish(p);
+  };
+
+  // one instance of the tile body (its code must stay small enough for the
+  // instruction cache): tile k fills y0, which is then parked in y1
+  for (int k = 0; k < nk; ++k) {
+    tile_body(k, y0, y1);
+#pragma unroll
+    for (int c = 0; c < kCBM; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y1[c][e] = y0[c][e];
+  }
+  tail(nk - 1, y1);
+
+  // ---- the last wave of the grid to finish resets the counters
+  wait_vmem();
+  unsigned old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(p.cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  if (old == gridDim.x * kNW - 1) {
+    const int ncnt = ngroups * kNW * kPSlots;
+    for (int c = lane; c < ncnt; c += kWave)
+      __hip_atomic_store(p.cnt + kPCntBase + c * kPCntStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(p.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -239,6 +239,38 @@ def test_config2_prefill_delayed_norm_sampled():
     assert np.array_equal(li_nn, mi.f32_to_bf16_bits(y32))
 
 
+@pytest.mark.parametrize("T", [2048, 2113, 3999])
+def test_persistent_delayed_every_token(T):
+    """Token counts served by the persistent delayed kernel (64-token tiles
+    over groups of 16 workgroups; several tiles per group, ragged last tile,
+    groups with unequal tile counts), checked on every token; without the
+    norm the layer input is the exact-order collapse, bit for bit."""
+    d = mi.pre_inputs(T, seed=40 + T, delayed=True, norm=True, outlier_frac=0.01)
+    say("persistent delayed T=%d" % T)
+    pre_out, post, comb, li = run_delayed(d)
+    o = oracle_delayed(d)
+    check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "persist T=%d" % T)
+    check_bf16(li, o["li_val"], o["li_mag"], what="persist T=%d layer_input" % T)
+    d2 = dict(d)
+    d2["norm_weight"] = None
+    _, _, _, li_nn = run_delayed(d2)
+    assert np.array_equal(li_nn, mi.f32_to_bf16_bits(oracle.collapse32(d["x"], d["pre_in"])))
+
+
+def test_persistent_repeat_and_workspace_reset():
+    """The persistent kernel's arrival counters are back at zero after every
+    call: calls of different sizes on one workspace repeat bit for bit."""
+    torch = torch_mod()
+    ds = {T: mi.pre_inputs(T, seed=800 + T, delayed=True, norm=True) for T in (4096, 2048)}
+    first = {T: run_delayed(ds[T]) for T in (4096, 2048)}
+    for T in (2048, 4096, 2048):
+        again = run_delayed(ds[T])
+        for u, v in zip(first[T], again):
+            assert np.array_equal(u, v)
+    ws = M.workspace(torch.device("cuda"), 4096, C)
+    assert int(ws[:4096].view(torch.int32).abs().sum()) == 0
+
+
 def test_config3_post_sampled():
     T = 16384
     p, post, comb = post_gates(T, seed=3)
