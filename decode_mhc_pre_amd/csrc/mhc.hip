@@ -50,8 +50,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout.
 //   split form:      counters [ntile] u32 (padded to 256 B), partials [ntile][nsplit][16][25] f32
 //   persistent form: word 0 finished waves, word 2 wait-budget flag, arrival counters
-//                    [group][wave][3] 256 B apart from word 64; records [group][wave][2]
-//                    (1 KB sum-y^2 block + 32 KB value block) from 64 KiB
+//                    [group][wave][5] 256 B apart from word 64; records [group][wave][4]
+//                    (1 KB sum-y^2 block + 32 KB value block) from 128 KiB
 size_t counter_bytes(const Plan& pl) { return align_up((size_t)pl.ntile * sizeof(unsigned), 256); }
 size_t plan_ws_bytes(const Plan& pl) {
   if (pl.persist) return persist_ws_bytes();

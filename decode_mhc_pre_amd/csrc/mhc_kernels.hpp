@@ -351,8 +351,7 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
 //   - after the last stream of a column block, the partial sum of squares of
 //     the collapsed row (folded RMSNorm).
 // The collapsed rows of a tile stay in registers until the norm factor is
-// known: two buffers, one filling while the previous tile's waits for the
-// rest of its group.
+// known: three buffers, the current tile's and the two before it.
 //
 // Exchange.  Each wave is in a group of 16 waves, the ones with its index in
 // the 16 members, sharing the same 16 tokens.  Its record per tile holds a
@@ -361,25 +360,31 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
 // projections and the row sum of squares of x, padded to a 128-byte line),
 // so that every store and load of the exchange moves whole lines: a member
 // writes 64 bytes and 2 KB, a reader loads 1 KB and its gate token's 2 KB.
-// At the end of tile k a wave stores its partial sums into record slot k & 1
-// and goes on without waiting.  The rest runs inside the next sweep, at fixed
-// steps, so that the x queue never drains:
-//   step kPQ:     increment slot k's arrival counter, once the first x load
+// A tile's partial sums leave the MFMA accumulators at the end of its sweep;
+// everything after that runs inside the next two sweeps, at fixed steps, so
+// that the x queue never drains.  During tile k + 1:
+//   steps 0-1:    store tile k's partial sums into record slot k % 4 (through
+//                 this wave's LDS transpose), without waiting;
+//   step 10:      increment slot k's arrival counter, once the first x load
 //                 issued after those stores has returned (vector memory
 //                 operations of a wave complete in issue order, so the stores
-//                 are complete as well);
-//   step 16:      read the counter; step 24: check it (only a member lagging
-//                 behind makes the wave wait) and load the group's records;
-//   step 32:      norm factors of the 16 tokens (every member sums the members'
-//                 partials in the same fixed order, so all hold the same bits)
-//                 and, over steps 32-39, the wave's columns of layer_input of
-//                 tile k from the parked buffer;
-//   step 32 on:   gates and Sinkhorn of one token (member r takes token r), one
-//                 iteration per step, written 21 steps later.
-// Slot k & 1 is rewritten at the end of tile k + 2, by which time every member
-// has consumed it: the writer checked at step 24 of tile k + 2 that every
-// member arrived for tile k + 1, which each does at step kPQ of tile k + 2,
-// after consuming tile k's records in tile k + 1.
+//                 are complete as well).
+// During tile k + 2, a whole tile after every member's arrival:
+//   step 4:       read the counter; step 12: check it (a wait here means a
+//                 member is a tile behind) and load the group's records;
+//   steps 19-21:  records through LDS; norm factors of the 16 tokens (every
+//                 member sums the members' partials in the same fixed order,
+//                 so all hold the same bits); the gate token's sums;
+//   steps 22-24:  gates of one token (member r takes token r), then one
+//                 Sinkhorn iteration per step, written at step 5 of the next
+//                 tile;
+//   steps 22-35:  the wave's columns of layer_input of tile k, one 32-column
+//                 block per step, from the oldest buffer.
+// The three row buffers move down one place block by block during a sweep,
+// just before the block's first write (parked buffers live in the AGPRs).
+// Slot k % 4 is rewritten during tile k + 5, after the writer checked (at step
+// 12 of tile k + 4) that every member arrived for tile k + 2, which each does
+// in tile k + 3, after consuming tile k's records in tile k + 2.
 // Counters only grow within a call (target = kPG x uses of the slot); the
 // last wave of the grid to finish sets them back to zero, so the workspace is
 // left as found.
@@ -402,7 +407,7 @@ constexpr int kPVals = 25;       // exchanged per token besides sum y^2: P[24], 
 constexpr int kPLine = 32;       // floats per (token, member) in the value block: one 128-byte line
 constexpr int kPSsy = kPG * kTileT;                    // floats of the sum-y^2 block
 constexpr int kPRec = kPSsy + kTileT * kPG * kPLine;   // floats per (group, wave, slot)
-constexpr int kPRing = 2;        // record slots per (group, wave)
+constexpr int kPRing = 4;        // record slots per (group, wave)
 // Workspace: word 0 counts finished waves, word 2 flags a wait that ran out of
 // budget; arrival counters from word kPCntBase, one per (group, wave, slot)
 // plus a scratch one (slot kPRing) for the first tile, each alone in its own
@@ -411,14 +416,22 @@ constexpr int kPRing = 2;        // record slots per (group, wave)
 constexpr int kPCntBase = 64;
 constexpr int kPCntStride = 64;  // words
 constexpr int kPSlots = kPRing + 1;
-constexpr size_t kPPartOffset = 64 * 1024;
+constexpr size_t kPPartOffset = 128 * 1024;
+static_assert(kPCntBase * 4 + (size_t)kPMaxGroups * (kThreads / kWave) * kPSlots * kPCntStride * 4 <= kPPartOffset,
+              "arrival counters overlap the records");
 constexpr int kSpinBudget = 1 << 20;  // sleeps per wave over the whole call (about a second)
-// steps of a tile at which the exchange of the previous tile advances
-constexpr int kPArrive = kPQ;    // arrive for the previous tile
-constexpr int kPCnt = 16;        // read its counter
-constexpr int kPCheck = 24;      // check it, load the records
-constexpr int kPUse = 32;        // norm factors, layer_input, Sinkhorn start
-constexpr int kPGateEnd = 13;    // step of the following tile at which the gates are written
+// steps of tile k at which the exchange of tiles k-1 and k-2 advances
+constexpr int kPPubA = 0;        // tile k-1: accumulators -> LDS transpose
+constexpr int kPPubB = 1;        //           LDS -> record stores
+constexpr int kPArrive = 10;     //           arrival (load 10 is the first issued after the stores)
+constexpr int kPCnt = 4;         // tile k-2: read the counter
+constexpr int kPCheck = 12;      //           check it, load the records
+constexpr int kPStage = 19;      //           records -> LDS
+constexpr int kPSumY = 20;       //           norm factors
+constexpr int kPSumG = 21;       //           the gate token's sums
+constexpr int kPInit = 22;       //           gates: logits, exponentials, sigmoids (3 steps)
+constexpr int kPIter = kPInit + 3;   //       Sinkhorn iterations from here, one per step
+constexpr int kPGateEnd = kPIter + 20 - 40;   // step of the following tile at which the gates are written
 
 inline size_t persist_ws_bytes() {
   return kPPartOffset + (size_t)kPMaxGroups * kNS * kPRing * kPRec * sizeof(float);
@@ -439,6 +452,24 @@ constexpr int kAuxAgent = 16;    // buffer cache policy: coherent at device scop
 __device__ __forceinline__ uint4 buf_load16_agent(rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAuxAgent));
 }
+// The accumulation registers (AGPRs) as parking space for values that wait a
+// tile or two: keeps the architectural registers free for the load queue.
+__device__ __forceinline__ float agpr_park(float v) {
+  float a;
+  __asm__("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
+  return a;
+}
+__device__ __forceinline__ float agpr_move(float a) {
+  float b;
+  __asm__("v_accvgpr_mov_b32 %0, %1" : "=a"(b) : "a"(a));
+  return b;
+}
+__device__ __forceinline__ float agpr_read(float a) {
+  float v;
+  __asm__("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 // An opaque zero that the compiler cannot compute before `v` is in a register:
 // whatever uses it waits for the load that produced `v`.
 __device__ __forceinline__ unsigned zero_after(unsigned v) {
@@ -458,23 +489,34 @@ struct TokenGates {
   int tok, it;
   bool write;
 
-  __device__ __forceinline__ void init(const PreParams& p, const float* v, const float* ba, int t,
-                                       bool w) {
+  // in three pieces (each a short dependent chain): logits, exponentials, gates
+  __device__ __forceinline__ void init_a(const PreParams& p, const float* v, const float* ba, int t,
+                                         bool w) {
     const int row = threadIdx.x & 3;
     const float r = 1.0f / sqrtf(v[24] / (float)p.K + p.eps);
     const float ac = ba[kNL + 2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) m[j] = ac * (r * v[8 + 4 * row + j]) + ba[8 + 4 * row + j];
-    const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] = expf(m[j] - mx);
-    const float lp = ba[kNL] * (r * v[row]) + ba[row];
-    const float lq = ba[kNL + 1] * (r * v[4 + row]) + ba[4 + row];
-    pr = 1.0f / (1.0f + expf(-lp));
-    po = 2.0f / (1.0f + expf(-lq));
+    pr = ba[kNL] * (r * v[row]) + ba[row];          // the pre logit, until init_c
+    po = ba[kNL + 1] * (r * v[4 + row]) + ba[4 + row];
     tok = t;
     it = 0;
     write = w;
+  }
+  __device__ __forceinline__ void init_b() {
+    const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = expf(m[j] - mx);
+  }
+  __device__ __forceinline__ void init_c() {
+    pr = 1.0f / (1.0f + expf(-pr));
+    po = 2.0f / (1.0f + expf(-po));
+  }
+  __device__ __forceinline__ void init(const PreParams& p, const float* v, const float* ba, int t,
+                                       bool w) {
+    init_a(p, v, ba, t, w);
+    init_b();
+    init_c();
   }
   __device__ __forceinline__ void step(int iters) {   // one Sinkhorn iteration, if any are left
     if (it < iters) {
@@ -562,10 +604,10 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   unsigned* cnt_base = p.cnt + kPCntBase + (grp * kNW + wave) * kPSlots * kPCntStride;
   float* rec_base = p.part + (size_t)(grp * kNW + wave) * kPRing * kPRec;
   // counter, arrival target and record of the group's k-th tile (k < 0: the scratch counter)
-  auto cnt_of = [&](int k) { return cnt_base + (k >= 0 ? (k & 1) : kPRing) * kPCntStride; };
-  auto target_of = [&](int k) { return k >= 0 ? (unsigned)kPG * (unsigned)((k >> 1) + 1) : 0u; };
+  auto cnt_of = [&](int k) { return cnt_base + (k >= 0 ? k % kPRing : kPRing) * kPCntStride; };
+  auto target_of = [&](int k) { return k >= 0 ? (unsigned)kPG * (unsigned)(k / kPRing + 1) : 0u; };
   auto rec_rsrc = [&](int k) {
-    return make_rsrc(rec_base + (size_t)(k >= 0 ? k & 1 : 0) * kPRec, k >= 0 ? kPRec * 4 : 0);
+    return make_rsrc(rec_base + (size_t)(k >= 0 ? k % kPRing : 0) * kPRec, k >= 0 ? kPRec * 4 : 0);
   };
 
   // ---- prologue: first x loads and pre_in, then the weight slice into LDS
@@ -595,9 +637,19 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   if (tid >= 32 && tid < 35) s_ba[kNL + tid - 32] = p.alpha[tid - 32];
   __syncthreads();
 
-  float y0[kCBM][8], y1[kCBM][8];
-  uint4 pv[3];      // the previous tile's records, in flight: sum-y^2 block, gate token's values
-  unsigned cv = 0;  // the previous tile's arrival counter
+  float y0[kCBM][8];                // the current tile's collapsed rows
+  float y1[kCBM][8], y2[kCBM][8];   // parked in AGPRs: the previous two tiles'
+#pragma unroll
+  for (int c = 0; c < kCBM; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y0[c][e] = 0.f;
+      y1[c][e] = y2[c][e] = agpr_park(0.f);
+    }
+  f32x4 pa0 = {0.f, 0.f, 0.f, 0.f}, pa1 = pa0, pa2 = pa0, pas = pa0;   // the last tile's accumulators
+  float pssy = 0.f;
+  uint4 pv[3];      // tile k-2's records, in flight: sum-y^2 block, gate token's values
+  unsigned cv = 0;  // tile k-2's arrival counter
   TokenGates gt;
   gt.m[0] = gt.m[1] = gt.m[2] = gt.m[3] = 1.0f;
   gt.pr = gt.po = 0.0f;
@@ -645,28 +697,37 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
     pv[1] = buf_load16_agent(rr, (kPSsy + mem * kPG * kPLine) * 4 + lane * 16, 0);
     pv[2] = buf_load16_agent(rr, (kPSsy + mem * kPG * kPLine) * 4 + (kWave + lane) * 16, 0);
   };
-  // norm factor of token i (returned) and the gate token's summed values (-> s_gv)
-  auto use_records = [&]() {
+  // the loaded records into this wave's LDS staging
+  auto stage_records = [&]() {
     s_xs[wave][lane] = __builtin_bit_cast(float4, pv[0]);
     s_xv[wave][lane] = __builtin_bit_cast(float4, pv[1]);
     s_xv[wave][kWave + lane] = __builtin_bit_cast(float4, pv[2]);
+  };
+  // norm factor of token i
+  auto sum_ssy = [&]() {
     const float* xs = reinterpret_cast<const float*>(s_xs[wave]);
-    const float* xv = reinterpret_cast<const float*>(s_xv[wave]);
     // token i, members 4g..4g+3, then the four groups: the same order in every member
     const float sg = ((xs[(4 * g) * kTileT + i] + xs[(4 * g + 1) * kTileT + i]) + xs[(4 * g + 2) * kTileT + i]) +
                      xs[(4 * g + 3) * kTileT + i];
     float sy = sg + __shfl_xor(sg, 16);
     sy = sy + __shfl_xor(sy, 32);
+    return norm ? 1.0f / sqrtf(sy / (float)kC + p.eps) : 1.0f;
+  };
+  // the gate token's summed values (-> s_gv), members in order
+  auto sum_gate = [&]() {
+    const float* xv = reinterpret_cast<const float*>(s_xv[wave]);
     if (lane < kPVals) {
       float acc = 0.f;
 #pragma unroll
       for (int m = 0; m < kPG; ++m) acc += xv[m * kPLine + lane];
       s_gv[wave][lane] = acc;
     }
-    return norm ? 1.0f / sqrtf(sy / (float)kC + p.eps) : 1.0f;
   };
-  auto li_store = [&](const float (&yb)[8], float ry, rsrc_t rl, int cb) {
-    float o[8];
+  // one 32-column block of layer_input; parked (AGPR) or live values
+  auto li_store = [&](const float (&yin)[8], bool parked, float ry, rsrc_t rl, int cb) {
+    float yb[8], o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) yb[e] = parked ? agpr_read(yin[e]) : yin[e];
     if (norm) {
       float w[8];
       unpack8(s_w[cb][g], w);
@@ -679,9 +740,55 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
     buf_store16(pack8(o), rl, llane + cb * kKB * 2, xsoff);
   };
 
-  // One tile: sweep of the group's k-th tile into ycur; exchange of tile k-1
-  // and its layer_input from yold.
-  auto tile_body = [&](int k, float (&ycur)[kCBM][8], float (&yold)[kCBM][8]) __attribute__((always_inline)) {
+  // the last tile's partial sums: accumulators (MFMA D layout) -> token rows in LDS
+  auto publish_a = [&]() {
+    float ssx = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (i == 4 * g + r) ssx = pas[r];
+    float t = pssy + __shfl_xor(pssy, 16);
+    t += __shfl_xor(t, 32);
+    float (*red)[52] = s_red[wave];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      red[4 * g + r][i] = pa0[r];
+      red[4 * g + r][16 + i] = pa1[r];
+      red[4 * g + r][32 + i] = pa2[r];
+    }
+    if ((i >> 2) == g) red[i][48] = ssx;
+    if (g == 0) red[i][49] = t;
+  };
+  // ... and -> record of the group's kk-th tile, whole lines, no wait
+  auto publish_b = [&](int kk) {
+    const float (*red)[52] = s_red[wave];
+    const rsrc_t rr = rec_rsrc(kk);
+    // value block: this member's line of each token, 128 chunks of 16 B (chunk
+    // c: token c >> 3, values 4 (c & 7) .. +3; P = hi + lo, then sum x^2, zeros)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = h * kWave + lane;
+      const int tt = c >> 3, v0 = 4 * (c & 7);
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = v0 + e;
+        o[e] = j < kNL ? red[tt][j] + red[tt][kNL + j] : j == kNL ? red[tt][48] : 0.f;
+      }
+      buf_store16_agent(make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                                   __float_as_uint(o[3])),
+                        rr, (kPSsy + (tt * kPG + mem) * kPLine + v0) * 4, 0);
+    }
+    // sum-y^2 block: this member's 16 tokens, 64 bytes
+    if (lane < 4)
+      buf_store16_agent(make_uint4(__float_as_uint(red[4 * lane][49]), __float_as_uint(red[4 * lane + 1][49]),
+                                   __float_as_uint(red[4 * lane + 2][49]), __float_as_uint(red[4 * lane + 3][49])),
+                        rr, (mem * kTileT + 4 * lane) * 4, 0);
+  };
+
+  // One tile: sweep of the group's k-th tile into ycur; exchange of tiles k-1
+  // and k-2, and tile k-2's layer_input from yold.
+  auto tile_body = [&](int k, float (&ycur)[kCBM][8], float (&y1)[kCBM][8], float (&y2)[kCBM][8])
+                       __attribute__((always_inline)) {
 #pragma clang fp contract(off)
     // re-define the base offsets in every tile, so that base + constant is
     // formed here (and folds into the instructions' offset fields) instead of
@@ -691,16 +798,21 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
     const rsrc_t rxn = x_rsrc(tnext);
     const float p0 = __uint_as_float(pq.x), p1 = __uint_as_float(pq.y);
     const float p2 = __uint_as_float(pq.z), p3 = __uint_as_float(pq.w);
-    const int t1 = tile_of(k - 1);
-    const rsrc_t rl1 = li_rsrc(t1);
     unsigned* cnt1 = cnt_of(k - 1);
-    const unsigned target1 = target_of(k - 1);
-    float ry1 = 1.0f;
+    const int t2 = tile_of(k - 2);
+    const rsrc_t rl2 = li_rsrc(t2);
+    unsigned* cnt2 = cnt_of(k - 2);
+    const unsigned target2 = target_of(k - 2);
+    float ry2 = 1.0f;
 
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, as = a0;
     float ssy = 0.f;
 #pragma unroll
     for (int n = 0; n < kLd; ++n) {
+      // Sinkhorn of the previous gate token: a chain of dependent arithmetic,
+      // first in the step so that it overlaps the wait for this step's x
+      if (n < kPGateEnd || n >= kPIter) gt.step(p.iters);
+      if (n == kPGateEnd) gt.finish(p);
       const uint4 xv = xq[n % kPQ];
       const int u = n / kUnit, q = n % kUnit;
       const int s = q >> 1, cb = 2 * u + (q & 1);
@@ -713,6 +825,16 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
       float f[8];
       unpack8(xv, f);
       const float ps = s == 0 ? p0 : s == 1 ? p1 : s == 2 ? p2 : p3;
+      if (s == 0) {
+        // the buffers move down one place, block by block, just before this
+        // tile's first write of the block: tile k-1's rows are parked, tile
+        // k-2's rows move to the oldest buffer
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y2[cb][e] = agpr_move(y1[cb][e]);
+          y1[cb][e] = agpr_park(ycur[cb][e]);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) ycur[cb][e] = s == 0 ? ps * f[e] : ycur[cb][e] + ps * f[e];
       if (s == kNS - 1) {
@@ -728,112 +850,78 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
         if (m == kLd) pq = buf_load16(pin_rsrc(tnext), plane, 0);
       }
       // ---- exchange of tile k-1
+      if (n == kPPubA) publish_a();
+      if (n == kPPubB) publish_b(k - 1);
       if (n == kPArrive) {
         // xv is the first x load issued after tile k-1's records were stored
         const unsigned z = zero_after(xv.x);
         if (lane == 0) __hip_atomic_fetch_add(cnt1, 1u + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      // ---- exchange of tile k-2 and its layer_input
       if (n == kPCnt) {
-        cv = ld_agent(cnt1);
+        cv = ld_agent(cnt2);
         __asm__ volatile("" ::: "memory");   // keep the read here, kPCheck - kPCnt steps ahead of its use
       }
       if (n == kPCheck) {
         cv += zero_after(xv.y);              // the check cannot move above this step
-        if ((int)(cv - target1) < 0) wait_count(cnt1, target1, cv);
-        load_records(k - 1);
-        __asm__ volatile("" ::: "memory");   // issued here, used kPUse - kPCheck steps later
+        if ((int)(cv - target2) < 0) wait_count(cnt2, target2, cv);
+        load_records(k - 2);
+        __asm__ volatile("" ::: "memory");   // issued here, used kPStage - kPCheck steps later
       }
-      if (n == kPUse) {
-        ry1 = use_records();
-        gt.init(p, s_gv[wave], s_ba, t1 * kPT + wave * kTileT + mem, t1 >= 0);
+      if (n == kPStage) stage_records();
+      if (n == kPSumY) ry2 = sum_ssy();
+      if (n == kPSumG) sum_gate();
+      if (n == kPInit) gt.init_a(p, s_gv[wave], s_ba, t2 * kPT + wave * kTileT + mem, t2 >= 0);
+      if (n == kPInit + 1) gt.init_b();
+      if (n == kPInit + 2) gt.init_c();
+      // layer_input of tile k-2, one block per step, each after its block moved
+      // to the oldest buffer (blocks 8 and 9 move at steps 32 and 33)
+      {
+        constexpr int kLiStep[kCBM] = {22, 23, 24, 25, 26, 27, 28, 29, 34, 35};
+#pragma unroll
+        for (int c = 0; c < kCBM; ++c)
+          if (n == kLiStep[c]) li_store(y2[c], true, ry2, rl2, c);
       }
-      if (n >= kPUse) {
-        // layer_input of tile k-1: ten column blocks over the last eight steps
-        const int c0 = n == kPUse ? 0 : n == kPUse + 1 ? 2 : n - kPUse + 2;
-        const int c1 = n == kPUse ? 2 : n == kPUse + 1 ? 4 : n - kPUse + 3;
-        for (int c = c0; c < c1 && c < kCBM; ++c) li_store(yold[c], ry1, rl1, c);
-        if (n > kPUse) gt.step(p.iters);
-      }
-      if (n < kPGateEnd) gt.step(p.iters);   // Sinkhorn of the previous gate token
-      if (n == kPGateEnd) gt.finish(p);
-      // keep every step's work in its step: the scheduler would otherwise sink
-      // the refill loads toward their use (shortening the queue) under the
-      // register pressure of the parked buffers
-      __builtin_amdgcn_sched_barrier(0);
     }
     rx = rxn;
 
-    // ---- this tile's partial sums -> record slot k & 1 (no wait)
-    {
-      float ssx = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (i == 4 * g + r) ssx = as[r];
-      float t = ssy + __shfl_xor(ssy, 16);
-      t += __shfl_xor(t, 32);
-      float (*red)[52] = s_red[wave];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        red[4 * g + r][i] = a0[r];
-        red[4 * g + r][16 + i] = a1[r];
-        red[4 * g + r][32 + i] = a2[r];
-      }
-      if ((i >> 2) == g) red[i][48] = ssx;
-      if (g == 0) red[i][49] = t;
-      const rsrc_t rr = rec_rsrc(k);
-      // value block: this member's line of each token, 128 chunks of 16 B (chunk
-      // c: token c >> 3, values 4 (c & 7) .. +3; P = hi + lo, then sum x^2, zeros)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = h * kWave + lane;
-        const int tt = c >> 3, v0 = 4 * (c & 7);
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = v0 + e;
-          o[e] = j < kNL ? red[tt][j] + red[tt][kNL + j] : j == kNL ? red[tt][48] : 0.f;
-        }
-        buf_store16_agent(make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
-                                     __float_as_uint(o[3])),
-                          rr, (kPSsy + (tt * kPG + mem) * kPLine + v0) * 4, 0);
-      }
-      // sum-y^2 block: this member's 16 tokens, 64 bytes
-      if (lane < 4)
-        buf_store16_agent(make_uint4(__float_as_uint(red[4 * lane][49]), __float_as_uint(red[4 * lane + 1][49]),
-                                     __float_as_uint(red[4 * lane + 2][49]), __float_as_uint(red[4 * lane + 3][49])),
-                          rr, (mem * kTileT + 4 * lane) * 4, 0);
-    }
+    pa0 = a0;
+    pa1 = a1;
+    pa2 = a2;
+    pas = as;
+    pssy = ssy;
   };
 
-  // After the last tile kl: its exchange and layer_input (buffer ylast),
-  // waiting as needed.
-  auto tail = [&](int kl, float (&ylast)[kCBM][8]) __attribute__((always_inline)) {
-    gt.finish(p);
-    wait_vmem();   // tile kl's records are stored
-    unsigned* c = cnt_of(kl);
-    if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // After the last tile kl: its partial sums, then the exchange and
+  // layer_input of tiles kl-1 (buffer y2) and kl (buffer y1), waiting as
+  // needed.
+  auto finish_tile = [&](int kk, const float (&yb)[kCBM][8], bool parked) __attribute__((always_inline)) {
+    unsigned* c = cnt_of(kk);
     const unsigned v = ld_agent(c);
-    if ((int)(v - target_of(kl)) < 0) wait_count(c, target_of(kl), v);
-    load_records(kl);
-    const float ry = use_records();
-    const int t = tile_of(kl);
-    gt.init(p, s_gv[wave], s_ba, t * kPT + wave * kTileT + mem, true);
+    if ((int)(v - target_of(kk)) < 0) wait_count(c, target_of(kk), v);
+    load_records(kk);
+    stage_records();
+    const float ry = sum_ssy();
+    sum_gate();
+    const int t = tile_of(kk);
+    gt.init(p, s_gv[wave], s_ba, t * kPT + wave * kTileT + mem, t >= 0);
     const rsrc_t rl = li_rsrc(t);
 #pragma unroll
-    for (int cb = 0; cb < kCBM; ++cb) li_store(ylast[cb], ry, rl, cb);
+    for (int cb = 0; cb < kCBM; ++cb) li_store(yb[cb], parked, ry, rl, cb);
     gt.finish(p);
   };
 
   // one instance of the tile body (its code must stay small enough for the
-  // instruction cache): tile k fills y0, which is then parked in y1
-  for (int k = 0; k < nk; ++k) {
-    tile_body(k, y0, y1);
-#pragma unroll
-    for (int c = 0; c < kCBM; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y1[c][e] = y0[c][e];
-  }
-  tail(nk - 1, y1);
+  // instruction cache); tile k fills y0 while y1, y2 hold tiles k-1, k-2
+  for (int k = 0; k < nk; ++k) tile_body(k, y0, y1, y2);
+  const int kl = nk - 1;
+  gt.finish(p);
+  publish_a();
+  publish_b(kl);
+  wait_vmem();   // tile kl's records are stored
+  if (lane == 0) __hip_atomic_fetch_add(cnt_of(kl), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (kl >= 1) finish_tile(kl - 1, y1, true);
+  finish_tile(kl, y0, false);
 
   // ---- the last wave of the grid to finish resets the counters
   wait_vmem();
