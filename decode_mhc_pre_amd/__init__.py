@@ -59,7 +59,9 @@ def lib() -> ctypes.CDLL:
         L.mhc_pre_delayed.argtypes = [P, P, I, I, I, _Weights, P, F, I, P, P, P, P, P, Z, P]
         L.mhc_post.argtypes = [P, P, P, P, I, I, I, P, P]
         L.mhc_broadcast_entry.argtypes = [P, I, I, I, _Weights, P, F, I, P, P, P, P, P, P, Z, P]
-        for f in ("mhc_pack_fn", "mhc_pre", "mhc_pre_delayed", "mhc_post", "mhc_broadcast_entry"):
+        L.mhc_collapse.argtypes = [P, P, I, I, I, P, F, P, P]
+        for f in ("mhc_pack_fn", "mhc_pre", "mhc_pre_delayed", "mhc_post", "mhc_broadcast_entry",
+                  "mhc_collapse"):
             getattr(L, f).restype = I
         L.mhc_status_str.argtypes = [I]
         L.mhc_status_str.restype = ctypes.c_char_p
@@ -68,7 +70,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("mhc_fn_packed_bytes", "mhc_pack_fn", "mhc_workspace_bytes", "mhc_pre",
-           "mhc_pre_delayed", "mhc_post", "mhc_broadcast_entry", "mhc_status_str")
+           "mhc_pre_delayed", "mhc_post", "mhc_broadcast_entry", "mhc_collapse", "mhc_status_str")
 
 
 def mhc_status_str(status: int) -> str:
@@ -201,6 +203,19 @@ def mhc_post(y, x, post, comb, out=None):
     st = lib().mhc_post(_ptr(_u16(y)), _ptr(_u16(x)), _ptr(post), _ptr(comb), T, n, C, _ptr(_u16(out)),
                         _stream(x.device))
     _check(st, "mhc_post")
+    return out
+
+
+def mhc_collapse(x, p, norm_weight=None, eps=1e-6, out=None):
+    """out [T,C] bf16 = exact-order collapse of x [T,4,C] with p [T,4] float32 (optional folded norm)."""
+    torch = _torch()
+    T, n, C = x.shape
+    if out is None:
+        out = torch.empty((T, C), dtype=torch.bfloat16, device=x.device)
+    st = lib().mhc_collapse(_ptr(_u16(x)), _ptr(p), T, n, C,
+                            _ptr(_u16(norm_weight)) if norm_weight is not None else None, float(eps),
+                            _ptr(_u16(out)), _stream(x.device))
+    _check(st, "mhc_collapse")
     return out
 
 

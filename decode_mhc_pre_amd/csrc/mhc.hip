@@ -308,6 +308,34 @@ mhc_status mhc_post(const uint16_t* y, const uint16_t* x, const float* post, con
   return launched();
 }
 
+mhc_status mhc_collapse(const uint16_t* x, const float* p, int T, int n, int C,
+                        const uint16_t* norm_weight, float eps, uint16_t* out, void* stream) {
+  mhc_status st = check_common(T, n, C);
+  if (st != MHC_OK) return st;
+  if (norm_weight && (!(eps >= 0.0f) || !std::isfinite(eps))) return MHC_ERR_SHAPE;
+  if (!x || !p || !out) return MHC_ERR_NULL;
+  const void* ptrs[] = {x, p, norm_weight, out};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MHC_ERR_ALIGN;
+  const size_t Tz = (size_t)T;
+  const Range ins[] = {{x, Tz * n * C * 2}, {p, Tz * 16}, {norm_weight, norm_weight ? (size_t)C * 2 : 0}};
+  const Range outs[] = {{out, Tz * C * 2}};
+  if (any_alias(outs, 1, ins, 3)) return MHC_ERR_ALIAS;
+  if (T == 0) return MHC_OK;
+  PreParams prm = {};
+  prm.x = x;
+  prm.pre_in = p;
+  prm.nw = norm_weight;
+  prm.li = out;
+  prm.eps = eps;
+  prm.T = T;
+  prm.C = C;
+  prm.K = n * C;
+  hipLaunchKernelGGL(mhc_collapse_kernel, dim3(T), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     prm);
+  return launched();
+}
+
 const char* mhc_status_str(mhc_status s) {
   switch (s) {
     case MHC_OK: return "MHC_OK";

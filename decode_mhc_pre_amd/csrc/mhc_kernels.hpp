@@ -10,6 +10,7 @@
 //                               over x per 64-token tile; projection (weight
 //                               slice resident in LDS), both sums of squares,
 //                               collapse and norm fused.
+//   mhc_collapse_kernel         standalone collapse (+ folded norm), one token per workgroup.
 //   mhc_post_kernel             post stage: post_i * y + sum_j comb_ij x_j.
 #pragma once
 
@@ -934,6 +935,16 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
       __hip_atomic_store(p.cnt + kPCntBase + c * kPCntStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane == 0) __hip_atomic_store(p.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// ------------------------------------------------------------------ standalone collapse
+// One workgroup per token: the exact-order collapse with p[token] and the
+// optional folded norm (collapse_norm_token), nothing else.
+__global__ __launch_bounds__(kThreads) void mhc_collapse_kernel(PreParams p) {
+  __shared__ float s_tmp[4];
+  const int tok = blockIdx.x;
+  const float4 pv = reinterpret_cast<const float4*>(p.pre_in)[tok];
+  collapse_norm_token<false>(p, tok, pv.x, pv.y, pv.z, pv.w, s_tmp);
 }
 
 // ------------------------------------------------------------------ post kernel

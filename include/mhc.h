@@ -147,6 +147,23 @@ mhc_status mhc_broadcast_entry(const uint16_t *h, int T, int n, int C,
                                uint16_t *layer_input, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Standalone collapse (p1 Result: the collapse also runs on its own at other
+ * call sites of the model, where no projection is needed):
+ *   x           [T][n][C] bf16    residual streams.
+ *   p           [T][n] float      mixing weights (a pre-mix).
+ *   norm_weight [C] bf16 or NULL  as in mhc_pre: NULL gives out = bf16(y);
+ *                                 otherwise out = bf16((y * ry) * w) with
+ *                                 ry = 1/sqrt(mean(y^2) + eps).
+ *   eps         >= 0 (used only with norm_weight).
+ *   out         [T][C] bf16 out   y_c = sum_i p_i x_{i,c}, each product rounded
+ *               to float and summed over i = 0..3 left to right: without the
+ *               norm, bit-identical to mhc_pre_delayed's layer_input for
+ *               pre_in = p.
+ * No workspace.  out must not overlap x, p or norm_weight (MHC_ERR_ALIAS). */
+mhc_status mhc_collapse(const uint16_t *x, const float *p, int T, int n, int C,
+                        const uint16_t *norm_weight, float eps, uint16_t *out,
+                        void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *mhc_status_str(mhc_status s);
 

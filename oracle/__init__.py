@@ -224,6 +224,14 @@ def mhc_pre_delayed(x_bits, pre_in, fn, bias, alpha, eps=1e-6, iters=20, norm_we
     return _finish_layer_input(x, p, norm_weight, eps, res)
 
 
+def mhc_collapse(x_bits, p, norm_weight=None, eps=1e-6):
+    """Standalone collapse (p1 Result: the collapse at its other call sites): steps 7-8
+    with the given float32 mixing weights p [T,4]."""
+    x = _c(x_bits, np.uint16)
+    pp = _c(p, np.float32).astype(np.float64)
+    return _finish_layer_input(x, pp, norm_weight, eps, {})
+
+
 def mhc_post(y_bits, x_bits, post, comb):
     y = _c(y_bits, np.uint16)
     x = _c(x_bits, np.uint16)

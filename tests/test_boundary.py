@@ -183,3 +183,25 @@ def test_pack_validation():
     f = P()
     assert L.mhc_pack_fn(f, 4 * C, f + 4096, None) == ALIAS
     assert L.mhc_pack_fn(P(), 4 * C, P(), None) == HIP
+
+
+def _collapse(x, p, T_, n, C_, nw, eps, out):
+    return m.lib().mhc_collapse(x, p, T_, n, C_, nw, eps, out, None)
+
+
+def test_collapse_validation():
+    P = Ptrs()
+    x, p, nw, out = P(), P(), P(), P()
+    assert _collapse(x, p, T, 3, C, nw, 1e-6, out) == UNSUP
+    assert _collapse(x, p, T, 4, 1000, nw, 1e-6, out) == UNSUP
+    assert _collapse(x, p, -1, 4, C, nw, 1e-6, out) == SHAPE
+    assert _collapse(x, p, T, 4, C, nw, -1.0, out) == SHAPE           # eps matters with a norm
+    assert _collapse(x, p, T, 4, C, None, -1.0, out) == HIP           # ... and is unused without
+    assert _collapse(None, p, T, 4, C, nw, 1e-6, out) == NULL
+    assert _collapse(x, None, T, 4, C, nw, 1e-6, out) == NULL
+    assert _collapse(x, p, T, 4, C, nw, 1e-6, None) == NULL
+    assert _collapse(x, p + 4, T, 4, C, nw, 1e-6, out) == ALIGN
+    assert _collapse(x, p, T, 4, C, nw, 1e-6, x + 64) == ALIAS
+    assert _collapse(x, p, T, 4, C, nw, 1e-6, p) == ALIAS
+    assert _collapse(x, p, 0, 4, C, nw, 1e-6, out) == OK
+    assert _collapse(x, p, T, 4, C, nw, 1e-6, out) == HIP

@@ -420,3 +420,24 @@ def test_delayed_gates_equal_non_delayed():
     c = oracle.mhc_pre_delayed(d["x"], a["pre"].astype(np.float32), d["fn"], d["bias"], d["alpha"],
                                norm_weight=d["norm_weight"])
     assert np.allclose(c["li_val"], a["li_val"], rtol=1e-6, atol=1e-6)
+
+
+def test_standalone_collapse_pins():
+    """The standalone collapse (p1 Result) is steps 7-8 alone: one-hot weights give
+    the stream back bit for bit; with w = 1 the folded norm has unit RMS; and it
+    agrees with the delayed pre's layer_input for pre_in = p."""
+    rng = np.random.default_rng(21)
+    T, C = 5, 512
+    x = _bits(rng.standard_normal((T, 4, C)))
+    for i in range(4):
+        p = np.zeros((T, 4), np.float32)
+        p[:, i] = 1.0
+        assert np.array_equal(oracle.mhc_collapse(x, p)["li"], x[:, i, :])
+    p = rng.uniform(0, 1, (T, 4)).astype(np.float32)
+    w1 = mi.f32_to_bf16_bits(np.ones(C, np.float32))
+    r = oracle.mhc_collapse(x, p, norm_weight=w1, eps=0.0)
+    rms = np.sqrt(np.mean(r["li_val"] ** 2, axis=1))
+    assert np.all(np.abs(rms - 1.0) < 1e-12)
+    fn = rng.standard_normal((4 * C, 24)) * 0.02
+    d = oracle.mhc_pre_delayed(x, p, fn, np.zeros(24), np.ones(3), 1e-6, 20, norm_weight=w1)
+    assert np.array_equal(oracle.mhc_collapse(x, p, norm_weight=w1)["li"], d["li"])

@@ -271,6 +271,31 @@ def test_persistent_repeat_and_workspace_reset():
     assert int(ws[:4096].view(torch.int32).abs().sum()) == 0
 
 
+@pytest.mark.parametrize("T", [1, 7, 300])
+def test_standalone_collapse(T):
+    """mhc_collapse: without the norm bit-exact to the exact-order float collapse;
+    with it within the bf16 bound of the oracle."""
+    rng = np.random.default_rng(60 + T)
+    d = mi.pre_inputs(T, seed=60 + T, delayed=True, norm=True)
+    p = rng.uniform(0, 1, (T, 4)).astype(np.float32)
+    x = dev_bf16(d["x"])
+    out = host_bits(M.mhc_collapse(x, dev_f32(p)))
+    assert np.array_equal(out, mi.f32_to_bf16_bits(oracle.collapse32(d["x"], p)))
+    outn = host_bits(M.mhc_collapse(x, dev_f32(p), dev_bf16(d["norm_weight"]), 1e-6))
+    o = oracle.mhc_collapse(d["x"], p, d["norm_weight"], 1e-6)
+    check_bf16(outn, o["li_val"], o["li_mag"], what="collapse T=%d" % T)
+
+
+@pytest.mark.parametrize("T", [100, 2113])
+def test_standalone_collapse_equals_delayed_layer_input(T):
+    """Without the norm, mhc_collapse(x, p) is bit-identical to the layer_input of
+    mhc_pre_delayed(x, pre_in = p), on both pre-kernel forms (split and persistent)."""
+    d = mi.pre_inputs(T, seed=70 + T, delayed=True, norm=False)
+    _, _, _, li = run_delayed(d)
+    out = host_bits(M.mhc_collapse(dev_bf16(d["x"]), dev_f32(d["pre_in"])))
+    assert np.array_equal(out, li)
+
+
 def test_config3_post_sampled():
     T = 16384
     p, post, comb = post_gates(T, seed=3)
