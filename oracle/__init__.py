@@ -16,6 +16,8 @@ gcc, loads it with ctypes and strings its steps together per operation:
 * :func:`mhc_post`           -- post * y + comb . x.
 * :func:`mhc_broadcast_entry`-- one stream broadcast to four, projected with the
                                 narrower entry weight (same PR, Summary/Approach).
+* :func:`mhc_post_pre_delayed` -- the post stage of one seam feeding the delayed
+                                pre stage of the next (cross-seam composition).
 
 Each returns exact values in float64 together with their bf16 roundings and the
 size of the summed terms (for error bounds).  Every function is pinned by tests
@@ -71,8 +73,9 @@ def lib():
         L.orc_collapse32.argtypes = [P, P, I64, I64, P]
         L.orc_norm.argtypes = [P, P, I64, I64, D, P, P]
         L.orc_post.argtypes = [P, P, P, P, I64, I64, P, P]
+        L.orc_post32.argtypes = [P, P, P, P, I64, I64, P]
         for name in ("orc_bf16_rne_array", "orc_logits", "orc_sinkhorn", "orc_gates",
-                     "orc_collapse64", "orc_collapse32", "orc_norm", "orc_post"):
+                     "orc_collapse64", "orc_collapse32", "orc_norm", "orc_post", "orc_post32"):
             getattr(L, name).restype = None
         _lib = L
     return _lib
@@ -242,6 +245,31 @@ def mhc_post(y_bits, x_bits, post, comb):
     mag = np.empty((T, NS, C))
     lib().orc_post(_ptr(y), _ptr(x), _ptr(post), _ptr(comb), T, C, _ptr(out), _ptr(mag))
     return dict(out_val=out, out_mag=mag, out=bf16_rne(out))
+
+
+def post32(y_bits, x_bits, post, comb):
+    """Post stage evaluated in single precision in the fixed order fl(post*y), then one
+    fused multiply-add per stream j = 0..3, rounded once to bf16: returns bits [T,4,C]."""
+    y = _c(y_bits, np.uint16)
+    x = _c(x_bits, np.uint16)
+    T, ns, C = x.shape
+    post = _c(post, np.float32).reshape(T, NS)
+    comb = _c(comb, np.float32).reshape(T, NS * NS)
+    out = np.empty((T, NS, C), dtype=np.uint16)
+    lib().orc_post32(_ptr(y), _ptr(x), _ptr(post), _ptr(comb), T, C, _ptr(out))
+    return out
+
+
+def mhc_post_pre_delayed(y_bits, x_bits, post_in, comb_in, pre_in, fn, bias, alpha, eps=1e-6, iters=20,
+                         norm_weight=None):
+    """Cross-seam composition: the post stage of seam k (gates post_in, comb_in) writes the
+    residual x_out, and the delayed pre stage of seam k+1 reads it, collapsing with
+    pre_in (seam k's pre-mix).  x_out is the single-precision post rounded once
+    (post32); everything after it is mhc_pre_delayed on those bits."""
+    xo = post32(y_bits, x_bits, post_in, comb_in)
+    res = mhc_pre_delayed(xo, pre_in, fn, bias, alpha, eps, iters, norm_weight=norm_weight)
+    res["x_out"] = xo
+    return res
 
 
 def mhc_broadcast_entry(h_bits, fn_e, bias, alpha, eps=1e-6, iters=20, norm_weight=None):

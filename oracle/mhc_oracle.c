@@ -25,8 +25,9 @@
  *   li_c  = bf16(y_c)  or  bf16((y_c * ry) * w_c), ry = 1/sqrt(sum y^2/C + eps)
  *   out_{i,c} = bf16(post_i y'_c + sum_j comb[i][j] x_{j,c})
  *
- * All floating point is IEEE double except orc_collapse32, which evaluates the
- * collapse in single precision in one fixed order.  Build with
+ * All floating point is IEEE double except orc_collapse32 and orc_post32, which
+ * evaluate the collapse and the post stage in single precision in one fixed
+ * order.  Build with
  * -O2 -fno-fast-math -ffp-contract=off so that no product is fused into an
  * addition and every rounding written here happens.
  *
@@ -286,6 +287,34 @@ void orc_post(const uint16_t *y, const uint16_t *x, const float *post,
                 out[(t * NS + i) * C + c] = acc;
                 if (mag)
                     mag[(t * NS + i) * C + c] = m;
+            }
+        }
+    }
+}
+
+/*
+ * Post stage in single precision, one fixed order, rounded once to bf16:
+ *   a = fl(post_i * y_c);  a = fma(comb[i][j], x_{j,c}, a) for j = 0, 1, 2, 3;
+ *   out[t][i][c] = bf16_rne(a).
+ * The next residual is a bf16 quantisation decided in single precision (p1
+ * Result: the post call sites produce the bf16 residual the next seam reads).
+ * When the next seam consumes it directly (cross-seam fusion), both sides take
+ * that rounding decision in the same precision and order, so the next seam's
+ * input is the same bits; orc_post gives the exact value it must stay within
+ * one bf16 ulp of.  fmaf is the correctly rounded C99 fused multiply-add.
+ */
+void orc_post32(const uint16_t *y, const uint16_t *x, const float *post,
+                const float *comb, int64_t T, int64_t C, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int i = 0; i < NS; ++i) {
+            const float pi = post[t * NS + i];
+            for (int64_t c = 0; c < C; ++c) {
+                volatile float a = pi * (float)bf16_val(y[t * C + c]);
+                for (int j = 0; j < NS; ++j)
+                    a = fmaf(comb[(t * NS + i) * NS + j], (float)bf16_val(x[(t * NS + j) * C + c]), a);
+                out[(t * NS + i) * C + c] = orc_bf16_rne((double)a);
             }
         }
     }

@@ -441,3 +441,78 @@ def test_standalone_collapse_pins():
     fn = rng.standard_normal((4 * C, 24)) * 0.02
     d = oracle.mhc_pre_delayed(x, p, fn, np.zeros(24), np.ones(3), 1e-6, 20, norm_weight=w1)
     assert np.array_equal(oracle.mhc_collapse(x, p, norm_weight=w1)["li"], d["li"])
+
+
+def test_post32_within_bar_identity_and_golden():
+    """Single-precision post (the residual the next seam reads): the identity gates
+    give x back; random gates stay within the bf16 bar of the exact value; the
+    hand-worked order case of tests/golden/post_order.txt."""
+    rng = np.random.default_rng(31)
+    T, C = 6, 512
+    y = _bits(rng.standard_normal((T, C)))
+    x = _bits(rng.standard_normal((T, 4, C)))
+    eye = np.tile(np.eye(4, dtype=np.float32), (T, 1, 1))
+    assert np.array_equal(oracle.post32(y, x, np.zeros((T, 4), np.float32), eye), x)
+    post = rng.uniform(0, 2, (T, 4)).astype(np.float32)
+    _, _, comb = oracle.gates(rng.standard_normal((T, 24)), 20)
+    comb32 = comb.astype(np.float32)
+    o32 = oracle.post32(y, x, post, comb32)
+    o = oracle.mhc_post(y, x, post, comb32)
+    v = o["out_val"]
+    a = np.abs(v)
+    ulp = np.exp2(np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7)
+    err = np.abs(oracle.bf16_to_f64(o32) - v)
+    assert np.all(err <= ulp + 6 * 2.0 ** -24 * o["out_mag"])
+    # mostly the correctly rounded bits; the rest one bf16 step away
+    assert np.mean(o32 == o["out"]) > 0.99
+    with open(os.path.join(GOLDEN, "post_order.txt")) as f:
+        rows = [ln for ln in f if ln.strip() and not ln.startswith("#")]
+    for ln in rows:
+        py, cr, xs, a_hex, b_hex, ex_hex = [s.strip() for s in ln.split("|")]
+        pv, yv = [float(s) for s in py.split()]
+        crow = np.float32([float(s) for s in cr.split()])
+        xv = np.float32([float(s) for s in xs.split()])
+        yb = mi.f32_to_bf16_bits(np.full((1, 8), yv, np.float32))
+        xb = mi.f32_to_bf16_bits(np.broadcast_to(xv[None, :, None], (1, 4, 8)).copy())
+        cm = np.zeros((1, 4, 4), np.float32)
+        cm[0, 0] = crow
+        pp = np.float32([[pv, 0, 0, 0]])
+        assert mi.bf16_bits_to_f32(yb)[0, 0] == yv and np.array_equal(mi.bf16_bits_to_f32(xb)[0, :, 0], xv)
+        out = oracle.post32(yb, xb, pp, cm)
+        assert out[0, 0, 0] == int(b_hex, 16)
+        ex = oracle.mhc_post(yb, xb, pp, cm)
+        assert ex["out_val"][0, 0, 0] == 1.0 + 2.0 ** -8 + 2.0 ** -23
+        assert ex["out"][0, 0, 0] == int(ex_hex, 16)
+        assert np.float32(np.float32(pv) * np.float32(yv)).view(np.uint32) == int(a_hex, 16)
+
+
+def test_post_pre_delayed_composition_pins():
+    """Cross-seam composition (post of seam k into the delayed pre of seam k+1):
+    with comb = I and post = 0 the residual passes through and everything equals
+    mhc_pre_delayed on x; with comb = 0 and post = 1 every stream becomes y, and the
+    gates equal the model-entry seam on y with the block-summed weight."""
+    T, Cs = 5, 256
+    d = mi.pre_inputs(T, seed=32, C=Cs, delayed=True, norm=True)
+    rng = np.random.default_rng(33)
+    y = _bits(rng.standard_normal((T, Cs)))
+    eye = np.tile(np.eye(4, dtype=np.float32), (T, 1, 1))
+    f = oracle.mhc_post_pre_delayed(y, d["x"], np.zeros((T, 4), np.float32), eye, d["pre_in"], d["fn"],
+                                    d["bias"], d["alpha"], norm_weight=d["norm_weight"])
+    g = oracle.mhc_pre_delayed(d["x"], d["pre_in"], d["fn"], d["bias"], d["alpha"], norm_weight=d["norm_weight"])
+    assert np.array_equal(f["x_out"], d["x"])
+    for k in ("pre_out", "post", "comb", "li"):
+        assert np.array_equal(f[k], g[k])
+    # multiples of 2^-10 keep fn and its block sums exact in float32
+    fn = (np.round(rng.standard_normal((4 * Cs, 24)) * 20.0) / 1024.0).astype(np.float32)
+    fn_e = fn.reshape(4, Cs, 24).sum(0, dtype=np.float64).astype(np.float32)
+    f = oracle.mhc_post_pre_delayed(y, d["x"], np.ones((T, 4), np.float32), np.zeros((T, 4, 4), np.float32),
+                                    d["pre_in"], fn, d["bias"], d["alpha"], norm_weight=d["norm_weight"])
+    assert np.array_equal(f["x_out"], np.repeat(y[:, None, :], 4, axis=1))
+    e = oracle.mhc_broadcast_entry(y, fn_e, d["bias"], d["alpha"], norm_weight=d["norm_weight"])
+    assert np.allclose(f["logits"], e["logits"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(f["pre_out"], e["pre"], rtol=1e-11, atol=1e-14)
+    assert np.allclose(f["comb"], e["comb"], rtol=1e-11, atol=1e-14)
+    # layer_input: the collapse of four copies of y with pre_in is (sum pre_in) * y
+    s = d["pre_in"].astype(np.float64).sum(1)
+    ybar = oracle.bf16_to_f64(y) * s[:, None]
+    assert np.allclose(f["y"], ybar, rtol=1e-12, atol=1e-12)
