@@ -7,8 +7,9 @@ the library's HIP kernels; there is no fallback path.  If the library is not
 built, importing the ops raises.
 
 Entry points (same names as the C ABI):
-    mhc_pack_fn, mhc_pre, mhc_pre_delayed, mhc_post, mhc_broadcast_entry,
-    mhc_workspace_bytes, mhc_fn_packed_bytes, mhc_status_str
+    mhc_pack_fn, mhc_pre, mhc_pre_delayed, mhc_post, mhc_post_pre_delayed,
+    mhc_broadcast_entry, mhc_collapse, mhc_workspace_bytes, mhc_fn_packed_bytes,
+    mhc_status_str
 """
 from __future__ import annotations
 
@@ -60,7 +61,9 @@ def lib() -> ctypes.CDLL:
         L.mhc_post.argtypes = [P, P, P, P, I, I, I, P, P]
         L.mhc_broadcast_entry.argtypes = [P, I, I, I, _Weights, P, F, I, P, P, P, P, P, P, Z, P]
         L.mhc_collapse.argtypes = [P, P, I, I, I, P, F, P, P]
-        for f in ("mhc_pack_fn", "mhc_pre", "mhc_pre_delayed", "mhc_post", "mhc_broadcast_entry",
+        L.mhc_post_pre_delayed.argtypes = [P, P, P, P, P, I, I, I, _Weights, P, F, I, P, P, P, P, P, P, Z, P]
+        for f in ("mhc_pack_fn", "mhc_pre", "mhc_pre_delayed", "mhc_post", "mhc_post_pre_delayed",
+                  "mhc_broadcast_entry",
                   "mhc_collapse"):
             getattr(L, f).restype = I
         L.mhc_status_str.argtypes = [I]
@@ -70,7 +73,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("mhc_fn_packed_bytes", "mhc_pack_fn", "mhc_workspace_bytes", "mhc_pre",
-           "mhc_pre_delayed", "mhc_post", "mhc_broadcast_entry", "mhc_collapse", "mhc_status_str")
+           "mhc_pre_delayed", "mhc_post", "mhc_post_pre_delayed", "mhc_broadcast_entry", "mhc_collapse",
+           "mhc_status_str")
 
 
 def mhc_status_str(status: int) -> str:
@@ -204,6 +208,27 @@ def mhc_post(y, x, post, comb, out=None):
                         _stream(x.device))
     _check(st, "mhc_post")
     return out
+
+
+def mhc_post_pre_delayed(y, x, post_in, comb_in, pre_in, w: Weights, norm_weight=None, eps=1e-6,
+                         iters=20, out=None, ws=None):
+    """Post stage of seam k (y [T,C], x [T,4,C], post_in [T,4], comb_in [T,4,4]) fused with the
+    delayed pre stage of seam k+1 (pre_in [T,4], weights w): returns (x_out [T,4,C], pre_out,
+    post, comb, layer_input).  x_out must be a separate buffer (not x)."""
+    torch = _torch()
+    T, n, C = x.shape
+    if out is None:
+        x_out = torch.empty_like(x)
+        pre, post, comb, li = _pre_outputs(T, C, x.device)
+    else:
+        x_out, pre, post, comb, li = out
+    ws = workspace(x.device, T, C) if ws is None else ws
+    st = lib().mhc_post_pre_delayed(_ptr(_u16(y)), _ptr(_u16(x)), _ptr(post_in), _ptr(comb_in), _ptr(pre_in),
+                                    T, n, C, w.as_c(), _ptr(_u16(norm_weight)), float(eps), int(iters),
+                                    _ptr(_u16(x_out)), _ptr(pre), _ptr(post), _ptr(comb), _ptr(li),
+                                    _ptr(ws), ws.numel(), _stream(x.device))
+    _check(st, "mhc_post_pre_delayed")
+    return x_out, pre, post, comb, li
 
 
 def mhc_collapse(x, p, norm_weight=None, eps=1e-6, out=None):

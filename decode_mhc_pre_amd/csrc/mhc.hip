@@ -118,21 +118,31 @@ mhc_status launched() {
   return e == hipSuccess ? MHC_OK : MHC_ERR_HIP;
 }
 
-// Shared by the three pre-stage entry points.
+// The previous seam's post-stage inputs of the fused form.
+struct PostIn {
+  const uint16_t* y;
+  const float* post;
+  const float* comb;
+};
+
+// Shared by the pre-stage entry points.
 mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, int n, int C,
                       mhc_weights w, const uint16_t* norm_weight, float eps, int iters,
                       uint16_t* x_out, float* pre, float* post, float* comb, uint16_t* li,
-                      void* ws, size_t ws_bytes, void* stream) {
+                      void* ws, size_t ws_bytes, void* stream, PostIn pi = {nullptr, nullptr, nullptr}) {
   mhc_status st = check_common(T, n, C);
   if (st != MHC_OK) return st;
   if ((st = check_scalars(eps, iters)) != MHC_OK) return st;
   const bool entry = mode == kModeEntry;
+  const bool fused = mode == kModeFused;
+  const bool delayed = mode == kModeDelayed || fused;
   if (!x || !w.fn_packed || !w.bias || !w.alpha || !pre || !post || !comb) return MHC_ERR_NULL;
-  if (mode == kModeDelayed && !pre_in) return MHC_ERR_NULL;
-  if (entry && !x_out) return MHC_ERR_NULL;
+  if (delayed && !pre_in) return MHC_ERR_NULL;
+  if ((entry || fused) && !x_out) return MHC_ERR_NULL;
+  if (fused && (!pi.y || !pi.post || !pi.comb)) return MHC_ERR_NULL;
   if (!entry && !li) return MHC_ERR_NULL;
   const void* ptrs[] = {x, pre_in, w.fn_packed, w.bias, w.alpha, norm_weight, x_out,
-                        pre, post, comb, li, ws};
+                        pre, post, comb, li, ws, pi.y, pi.post, pi.comb};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MHC_ERR_ALIGN;
 
@@ -140,18 +150,21 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   const int KB = K / kKB;
   const size_t Tz = (size_t)T;
   const Range ins[] = {{x, Tz * K * 2},
-                       {pre_in, mode == kModeDelayed ? Tz * 16 : 0},
+                       {pre_in, delayed ? Tz * 16 : 0},
                        {w.fn_packed, mhc_fn_packed_bytes(K)},
                        {w.bias, 96},
                        {w.alpha, 12},
-                       {norm_weight, norm_weight ? (size_t)C * 2 : 0}};
+                       {norm_weight, norm_weight ? (size_t)C * 2 : 0},
+                       {pi.y, fused ? Tz * C * 2 : 0},
+                       {pi.post, fused ? Tz * 16 : 0},
+                       {pi.comb, fused ? Tz * 64 : 0}};
   const Range outs[] = {{pre, Tz * 16},
                         {post, Tz * 16},
                         {comb, Tz * 64},
                         {li, li ? Tz * C * 2 : 0},
-                        {x_out, entry ? Tz * n * C * 2 : 0},
+                        {x_out, (entry || fused) ? Tz * n * C * 2 : 0},
                         {ws, ws ? ws_bytes : 0}};
-  if (any_alias(outs, 6, ins, 6)) return MHC_ERR_ALIAS;
+  if (any_alias(outs, 6, ins, 9)) return MHC_ERR_ALIAS;
 
   if (T == 0) return MHC_OK;
   Plan pl = make_plan(T, KB, mode == kModeDelayed && C == kGroupC);
@@ -170,6 +183,9 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   p.comb = comb;
   p.li = li;
   p.xout = x_out;
+  p.ysub = pi.y;
+  p.post_in = pi.post;
+  p.comb_in = pi.comb;
   p.cnt = need ? static_cast<unsigned*>(ws) : nullptr;
   p.part = need ? reinterpret_cast<float*>(static_cast<char*>(ws) +
                                            (pl.persist ? kPPartOffset : counter_bytes(pl)))
@@ -207,6 +223,9 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
       break;
     case kModeDelayed:
       hipLaunchKernelGGL(mhc_pre_split_kernel<kModeDelayed>, dim3(pl.nproj + T), block, 0, s, p);
+      break;
+    case kModeFused:
+      hipLaunchKernelGGL(mhc_pre_split_kernel<kModeFused>, dim3(pl.nproj + T), block, 0, s, p);
       break;
     default:
       hipLaunchKernelGGL(mhc_pre_split_kernel<kModeEntry>, dim3(pl.nproj), block, 0, s, p);
@@ -279,6 +298,17 @@ mhc_status mhc_broadcast_entry(const uint16_t* h, int T, int n, int C, mhc_weigh
                                void* stream) {
   return pre_common(kModeEntry, h, nullptr, T, n, C, w_entry, norm_weight, eps, sinkhorn_iters,
                     x_out, pre, post, comb, layer_input, workspace, workspace_bytes, stream);
+}
+
+mhc_status mhc_post_pre_delayed(const uint16_t* y, const uint16_t* x, const float* post_in,
+                                const float* comb_in, const float* pre_in, int T, int n, int C,
+                                mhc_weights w, const uint16_t* norm_weight, float eps,
+                                int sinkhorn_iters, uint16_t* x_out, float* pre_out, float* post,
+                                float* comb, uint16_t* layer_input, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return pre_common(kModeFused, x, pre_in, T, n, C, w, norm_weight, eps, sinkhorn_iters, x_out,
+                    pre_out, post, comb, layer_input, workspace, workspace_bytes, stream,
+                    PostIn{y, post_in, comb_in});
 }
 
 mhc_status mhc_post(const uint16_t* y, const uint16_t* x, const float* post, const float* comb,

@@ -130,6 +130,29 @@ __device__ __forceinline__ void collapse8(const uint4& v0, const uint4& v1, cons
   for (int e = 0; e < 8; ++e) y[e] = collapse1(p0, p1, p2, p3, a[e], b[e], c[e], d[e]);
 }
 
+// ---------------------------------------------------------------- post stage
+// Residual stream i of the post stage for 8 hidden elements:
+//   a = fl(post_i * y);  a = fma(comb[i][j], x_j, a) for j = 0, 1, 2, 3;  bf16(a)
+// (single precision, this order, one rounding).  Every kernel that writes or
+// consumes the next residual uses this one definition, so the bf16 residual
+// the next seam reads is the same bits whichever kernel produced it.
+__device__ __forceinline__ uint4 post_stream8(float pw, float c0, float c1, float c2, float c3,
+                                              const float (&y)[8], const float (&x0)[8],
+                                              const float (&x1)[8], const float (&x2)[8],
+                                              const float (&x3)[8]) {
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float a = pw * y[e];
+    a = __builtin_fmaf(c0, x0[e], a);
+    a = __builtin_fmaf(c1, x1[e], a);
+    a = __builtin_fmaf(c2, x2[e], a);
+    a = __builtin_fmaf(c3, x3[e], a);
+    o[e] = a;
+  }
+  return pack8(o);
+}
+
 // ---------------------------------------------------------------- reductions
 // Butterfly over all 64 lanes: every lane ends with the same bits (float
 // addition is commutative, so partner lanes form identical sums).

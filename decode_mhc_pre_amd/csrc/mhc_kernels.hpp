@@ -18,7 +18,7 @@
 
 namespace mhc {
 
-enum Mode { kModePre = 0, kModeDelayed = 1, kModeEntry = 2 };
+enum Mode { kModePre = 0, kModeDelayed = 1, kModeEntry = 2, kModeFused = 3 };
 
 struct PreParams {
   const uint16_t* x;      // [T][K] bf16: residual [T][4][C] flattened, or h [T][C] (entry)
@@ -31,7 +31,10 @@ struct PreParams {
   float* post;            // [T][4]
   float* comb;            // [T][16]
   uint16_t* li;           // [T][C] layer_input (entry: may be nullptr)
-  uint16_t* xout;         // [T][4][C] broadcast residual (entry)
+  uint16_t* xout;         // [T][4][C] broadcast residual (entry) / next residual (fused)
+  const uint16_t* ysub;   // [T][C] sublayer output (fused)
+  const float* post_in;   // [T][4] post gates of the previous seam (fused)
+  const float* comb_in;   // [T][16] comb of the previous seam (fused)
   float* part;            // workspace: partial sums [ntile][nsplit][16][25]
   unsigned* cnt;          // workspace: arrival counters [ntile]
   float eps;
@@ -117,7 +120,10 @@ __device__ __forceinline__ void tile_gates(const PreParams& p, const float (*s_P
 // ------------------------------------------------------------------ collapse + norm, one token
 // The whole 256-thread workgroup handles token `tok`: y (float) stays in
 // registers, sum(y^2) is reduced over the workgroup, then layer_input is written.
-template <bool kBcast>
+// kPost: the streams collapsed are the post stage's output, computed here from
+// the previous residual, the sublayer output and the previous seam's gates,
+// and written out as the next residual on the way.
+template <bool kBcast, bool kPost = false>
 __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok, float p0, float p1,
                                                     float p2, float p3, float* s_tmp) {
   const int C8 = p.C >> 3;
@@ -125,16 +131,44 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
   uint4* lo = reinterpret_cast<uint4*>(p.li) + (size_t)tok * C8;
   const uint4* w8 = reinterpret_cast<const uint4*>(p.nw);
   const bool norm = p.nw != nullptr;
+  float pw[4] = {0.f, 0.f, 0.f, 0.f};
+  float4 cr[4];
+  if (kPost) {
+    const float4 pg = reinterpret_cast<const float4*>(p.post_in)[tok];
+    pw[0] = pg.x;
+    pw[1] = pg.y;
+    pw[2] = pg.z;
+    pw[3] = pg.w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cr[i] = reinterpret_cast<const float4*>(p.comb_in)[(size_t)tok * 4 + i];
+  }
   float y[8][8];
   float ss = 0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int c8 = threadIdx.x + s * kThreads;
     if (c8 < C8) {
-      const uint4 v0 = xs[c8];
-      const uint4 v1 = kBcast ? v0 : xs[C8 + c8];
-      const uint4 v2 = kBcast ? v0 : xs[2 * C8 + c8];
-      const uint4 v3 = kBcast ? v0 : xs[3 * C8 + c8];
+      uint4 v0 = xs[c8];
+      uint4 v1 = kBcast ? v0 : xs[C8 + c8];
+      uint4 v2 = kBcast ? v0 : xs[2 * C8 + c8];
+      uint4 v3 = kBcast ? v0 : xs[3 * C8 + c8];
+      if (kPost) {
+        float yv[8], a0[8], a1[8], a2[8], a3[8];
+        unpack8(reinterpret_cast<const uint4*>(p.ysub)[(size_t)tok * C8 + c8], yv);
+        unpack8(v0, a0);
+        unpack8(v1, a1);
+        unpack8(v2, a2);
+        unpack8(v3, a3);
+        v0 = post_stream8(pw[0], cr[0].x, cr[0].y, cr[0].z, cr[0].w, yv, a0, a1, a2, a3);
+        v1 = post_stream8(pw[1], cr[1].x, cr[1].y, cr[1].z, cr[1].w, yv, a0, a1, a2, a3);
+        v2 = post_stream8(pw[2], cr[2].x, cr[2].y, cr[2].z, cr[2].w, yv, a0, a1, a2, a3);
+        v3 = post_stream8(pw[3], cr[3].x, cr[3].y, cr[3].z, cr[3].w, yv, a0, a1, a2, a3);
+        uint4* xo = reinterpret_cast<uint4*>(p.xout) + (size_t)tok * kNS * C8 + c8;
+        xo[0] = v0;
+        xo[C8] = v1;
+        xo[2 * C8] = v2;
+        xo[3 * C8] = v3;
+      }
       collapse8(v0, v1, v2, v3, p0, p1, p2, p3, y[s]);
       if (norm) {
 #pragma unroll
@@ -167,6 +201,12 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
 // delayed, the collapse.  Delayed only: workgroups [nproj, nproj + T) collapse
 // one token each with the carried pre-mix; they need nothing from the
 // projection, so no workgroup ever waits for another.
+// Fused (post of the previous seam, then the delayed pre): the projection
+// splits the hidden columns instead of the 4C row, so that each 32-column
+// block's five loads (sublayer output, four residual streams) give all four
+// next-residual fragments; the collapse workgroups recompute the token's next
+// residual with the same arithmetic (same bits) and are the ones that write it.
+constexpr int kJFused = 2;   // column blocks a wave loads together in the fused projection
 template <int MODE>
 __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   __shared__ float s_red[4][kTileT][52];   // per-wave partial D (48 cols) + sumsq
@@ -178,10 +218,10 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
 
-  if (MODE == kModeDelayed && b >= p.nproj) {
+  if ((MODE == kModeDelayed || MODE == kModeFused) && b >= p.nproj) {
     const int tok = b - p.nproj;
     const float4 pin = reinterpret_cast<const float4*>(p.pre_in)[tok];
-    collapse_norm_token<false>(p, tok, pin.x, pin.y, pin.z, pin.w, &s_tmp[0]);
+    collapse_norm_token<false, MODE == kModeFused>(p, tok, pin.x, pin.y, pin.z, pin.w, &s_tmp[0]);
     return;
   }
 
@@ -203,6 +243,63 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
   float ssq = 0.f;
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (MODE == kModeFused) {
+    // column blocks [cbA, cbB) of all four streams; wave w takes cbA + w, +4, ...
+    const int CB = p.C / kKB;
+    const int cbA = (int)(((long long)sp * CB) / p.nsplit);
+    const int cbB = (int)(((long long)(sp + 1) * CB) / p.nsplit);
+    const uint16_t* yrow = p.ysub + (size_t)(valid ? tok : 0) * p.C + g * 8;
+    float pw[4] = {0.f, 0.f, 0.f, 0.f};
+    float4 cr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) cr[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (valid) {
+      const float4 pg = reinterpret_cast<const float4*>(p.post_in)[tok];
+      pw[0] = pg.x;
+      pw[1] = pg.y;
+      pw[2] = pg.z;
+      pw[3] = pg.w;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) cr[s] = reinterpret_cast<const float4*>(p.comb_in)[(size_t)tok * 4 + s];
+    }
+    for (int base = cbA + wave; base < cbB; base += 4 * kJFused) {
+      uint4 yv[kJFused], xv[kJFused][kNS], bw[kJFused][kNS][kFragPerKB];
+#pragma unroll
+      for (int j = 0; j < kJFused; ++j) {
+        const int cb = base + 4 * j;
+        if (cb < cbB) {
+          yv[j] = valid ? *reinterpret_cast<const uint4*>(yrow + (size_t)cb * kKB) : zero;
+#pragma unroll
+          for (int s = 0; s < kNS; ++s) {
+            xv[j][s] = valid ? *reinterpret_cast<const uint4*>(xrow + (size_t)s * p.C + (size_t)cb * kKB) : zero;
+            const uint4* bp = p.fnp + (size_t)(s * CB + cb) * (kFragPerKB * kWave) + lane;
+#pragma unroll
+            for (int f = 0; f < kFragPerKB; ++f) bw[j][s][f] = bp[f * kWave];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kJFused; ++j) {
+        const int cb = base + 4 * j;
+        if (cb < cbB) {
+          float yf[8], x0[8], x1[8], x2[8], x3[8];
+          unpack8(yv[j], yf);
+          unpack8(xv[j][0], x0);
+          unpack8(xv[j][1], x1);
+          unpack8(xv[j][2], x2);
+          unpack8(xv[j][3], x3);
+#pragma unroll
+          for (int s = 0; s < kNS; ++s) {
+            const uint4 xn = post_stream8(pw[s], cr[s].x, cr[s].y, cr[s].z, cr[s].w, yf, x0, x1, x2, x3);
+            ssq += sumsq8(xn);
+            acc0 = mfma_bf16(xn, bw[j][s][0], acc0);
+            acc1 = mfma_bf16(xn, bw[j][s][1], acc1);
+            acc2 = mfma_bf16(xn, bw[j][s][2], acc2);
+          }
+        }
+      }
+    }
+  } else
   for (int base = kb0 + wave; base < kb1; base += 4 * kJMax) {
     uint4 xv[kJMax], b0[kJMax], b1[kJMax], b2[kJMax];
 #pragma unroll
@@ -320,7 +417,7 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
 
   if (wave == 0) tile_gates(p, s_P, t0, s_pre);
 
-  if (MODE == kModeDelayed || p.li == nullptr) return;
+  if (MODE == kModeDelayed || MODE == kModeFused || p.li == nullptr) return;
   __syncthreads();
   // ---- collapse with this seam's own pre-mix, token by token
   const int nt = min(kTileT, p.T - t0);
@@ -979,19 +1076,9 @@ __global__ __launch_bounds__(256) void mhc_post_kernel(const uint4* __restrict__
   unpack8(q3, x3);
   const float pw[4] = {pg.x, pg.y, pg.z, pg.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float a = pw[i] * yv[e];
-      a = __builtin_fmaf(cr[i].x, x0[e], a);
-      a = __builtin_fmaf(cr[i].y, x1[e], a);
-      a = __builtin_fmaf(cr[i].z, x2[e], a);
-      a = __builtin_fmaf(cr[i].w, x3[e], a);
-      o[e] = a;
-    }
-    nt_store16(pack8(o), out + xb + (size_t)i * C8);
-  }
+  for (int i = 0; i < 4; ++i)
+    nt_store16(post_stream8(pw[i], cr[i].x, cr[i].y, cr[i].z, cr[i].w, yv, x0, x1, x2, x3),
+               out + xb + (size_t)i * C8);
 }
 
 }  // namespace mhc

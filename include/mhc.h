@@ -132,6 +132,36 @@ mhc_status mhc_post(const uint16_t *y, const uint16_t *x, const float *post,
                     const float *comb, int T, int n, int C, uint16_t *out,
                     void *stream);
 
+/* Cross-seam fused form: the post stage of seam k and the delayed pre stage
+ * of seam k+1 in one pass over the residual (p1 Notes / follow-ups: fewer
+ * launches per seam; the delayed form makes it possible because the pre-mix
+ * that collapses seam k+1 is seam k's, known before the pass).  The results
+ * are those of mhc_post(y, x, post_in, comb_in) -> x_out followed by
+ * mhc_pre_delayed(x_out, pre_in, ...): x_out and layer_input bit for bit, the
+ * gates up to the order in which the projection's partial sums are added:
+ *   y        [T][C] bf16      sublayer output of seam k.
+ *   x        [T][n][C] bf16   residual entering seam k.
+ *   post_in  [T][n] float     seam k's post gates; comb_in [T][n][n] float its comb.
+ *   pre_in   [T][n] float     seam k's pre-mix, which collapses seam k+1.
+ *   w, norm_weight, eps, sinkhorn_iters: seam k+1's, as in mhc_pre_delayed.
+ *   x_out    [T][n][C] bf16 out  the residual entering seam k+1,
+ *            bf16(post_i y + sum_j comb_in[i][j] x_j) evaluated in float as
+ *            fl(post_i y) followed by one fused multiply-add per j in order and
+ *            rounded once (the same bits as mhc_post).
+ *   pre_out, post, comb, layer_input: seam k+1's outputs, from x_out, as in
+ *            mhc_pre_delayed.
+ * The workspace is that of mhc_pre_delayed (mhc_workspace_bytes).  x_out must
+ * not overlap x or any other argument: this form is not in place
+ * (MHC_ERR_ALIAS). */
+mhc_status mhc_post_pre_delayed(const uint16_t *y, const uint16_t *x,
+                                const float *post_in, const float *comb_in,
+                                const float *pre_in, int T, int n, int C,
+                                mhc_weights w, const uint16_t *norm_weight,
+                                float eps, int sinkhorn_iters, uint16_t *x_out,
+                                float *pre_out, float *post, float *comb,
+                                uint16_t *layer_input, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 /* Model-entry seam (p1 Summary and Approach: the broadcast seam projects a
  * narrower operand).  The single stream h[T][C] bf16 is broadcast to all n
  * streams, x_out[t][i][:] = h[t][:]; the logits come from h . fn_e with the

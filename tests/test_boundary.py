@@ -82,6 +82,17 @@ def call_pre(**kw):
                            a["pre"], a["post"], a["comb"], a["li"], a["ws"], a["ws_bytes"], None)
 
 
+def call_fused(**kw):
+    a = _pre_args(**kw)
+    P = Ptrs()
+    P.next = 0x80000000000
+    for k in ("y", "post_in", "comb_in", "xo"):
+        a.setdefault(k, kw.get(k, P()))
+    return m.lib().mhc_post_pre_delayed(a["y"], a["x"], a["post_in"], a["comb_in"], a["pre_in"], a["T"], a["n"],
+                                        a["C"], a["w"], a["nw"], a["eps"], a["iters"], a["xo"], a["pre"], a["post"],
+                                        a["comb"], a["li"], a["ws"], a["ws_bytes"], None)
+
+
 def call_entry(**kw):
     a = _pre_args(**kw)
     xo = a.get("xo", Ptrs().__call__() + (1 << 40))
@@ -90,7 +101,7 @@ def call_entry(**kw):
                                        None)
 
 
-@pytest.mark.parametrize("call", [call_pre, call_delayed, call_entry])
+@pytest.mark.parametrize("call", [call_pre, call_delayed, call_entry, call_fused])
 def test_pre_validation(call):
     assert call(n=3) == UNSUP
     assert call(C=5000) == UNSUP
@@ -128,6 +139,24 @@ def test_delayed_specific():
     assert call_delayed(pre=pre, ws=pre) == ALIAS
     # pre_out must not overlap the carried pre_in
     assert call_delayed(pre_in=pre, pre=pre) == ALIAS
+
+
+def test_fused_specific():
+    for k in ("y", "post_in", "comb_in", "xo", "pre_in", "li"):
+        assert call_fused(**{k: None}) == NULL, k
+    assert call_fused(post_in=0x80000000004) == ALIGN
+    P = Ptrs()
+    x = P()
+    assert call_fused(x=x, xo=x) == ALIAS                      # not in place
+    assert call_fused(x=x, xo=x + T * 4 * C * 2) != ALIAS      # adjacent is fine (then: no GPU)
+    y = P()
+    assert call_fused(y=y, li=y) == ALIAS
+    g = P()
+    assert call_fused(post_in=g, post=g) == ALIAS              # this seam's gates are new buffers
+    assert call_fused(comb_in=g, comb=g + 32) == ALIAS
+    assert call_fused(pre_in=g, pre=g) == ALIAS
+    assert call_fused(T=0) == OK
+    assert call_fused() == HIP
 
 
 def test_entry_specific():

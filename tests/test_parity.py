@@ -200,6 +200,23 @@ def test_post_small(T):
     assert np.array_equal(host_bits(x), host_bits(out))
 
 
+def test_post_bits_equal_single_precision_oracle():
+    """mhc_post writes the single-precision post rounded once (the residual the next
+    seam reads), bit for bit, and the hand-worked order case of
+    tests/golden/post_order.txt."""
+    T = 33
+    p, post, comb = post_gates(T, seed=41)
+    out = M.mhc_post(dev_bf16(p["y"]), dev_bf16(p["x"]), dev_f32(post), dev_f32(comb))
+    assert np.array_equal(host_bits(out), oracle.post32(p["y"], p["x"], post, comb))
+    yb = np.full((1, C), 0x3F80, np.uint16)
+    xb = np.full((1, 4, C), 0x3F80, np.uint16)
+    pp = np.float32([[1.0 + 2.0 ** -8, 0, 0, 0]])
+    cm = np.zeros((1, 4, 4), np.float32)
+    cm[0, 0] = 2.0 ** -25
+    out = M.mhc_post(dev_bf16(yb), dev_bf16(xb), dev_f32(pp), dev_f32(cm))
+    assert np.all(host_bits(out)[0, 0] == 0x3F80)
+
+
 def test_post_identity():
     torch = torch_mod()
     T = 5
@@ -321,3 +338,65 @@ def test_repeatable_and_workspace_reset():
     ws = M.workspace(torch.device("cuda"), 1, C)
     n_cnt = 256
     assert int(ws[: 4 * n_cnt].view(torch.int32).abs().sum()) == 0
+
+
+# ----------------------------------------------------------------------------- post -> delayed pre, fused
+
+def fused_case(T, seed, norm=True, outlier_frac=0.0):
+    """Seam k's post inputs (y, gates) and seam k+1's delayed pre inputs (x = the
+    residual entering seam k, weights, pre_in = seam k's pre-mix)."""
+    d = mi.pre_inputs(T, seed=seed, delayed=True, norm=norm, outlier_frac=outlier_frac)
+    p, post, comb = post_gates(T, seed=seed + 1)
+    return d, p["y"], post, comb
+
+
+def run_fused(d, y, post, comb, rows=None):
+    nw = dev_bf16(d["norm_weight"]) if d["norm_weight"] is not None else None
+    xo, pre_out, po, co, li = M.mhc_post_pre_delayed(dev_bf16(y), dev_bf16(d["x"]), dev_f32(post), dev_f32(comb),
+                                                     dev_f32(d["pre_in"]), weights(d), nw, d["eps"], d["iters"])
+    torch_mod().cuda.synchronize()
+    r = slice(None) if rows is None else rows
+    return host_bits(xo)[r], host_f32(pre_out)[r], host_f32(po)[r], host_f32(co)[r], host_bits(li)[r]
+
+
+def check_fused(got, d, y, post, comb, rows=None, what=""):
+    r = slice(None) if rows is None else rows
+    xo, pre_out, po, co, li = got
+    o = oracle.mhc_post_pre_delayed(y[r], d["x"][r], post[r], comb[r], d["pre_in"][r], d["fn"], d["bias"],
+                                    d["alpha"], d["eps"], d["iters"], norm_weight=d["norm_weight"])
+    # the next residual: the single-precision post bit for bit, within the bar of the exact one
+    assert np.array_equal(xo, o["x_out"]), what
+    ex = oracle.mhc_post(y[r], d["x"][r], post[r], comb[r])
+    check_bf16(xo, ex["out_val"], ex["out_mag"], what=what + " x_out")
+    check_gates(pre_out, po, co, o["pre_out"], o["post"], o["comb"], what)
+    if d["norm_weight"] is None:
+        assert np.array_equal(li, mi.f32_to_bf16_bits(oracle.collapse32(o["x_out"], d["pre_in"][r]))), what
+    check_bf16(li, o["li_val"], o["li_mag"], what=what + " layer_input")
+
+
+@pytest.mark.parametrize("T,norm", [(1, True), (2, False), (7, True), (16, False), (128, True), (300, True),
+                                    (1000, False)])
+def test_post_pre_delayed(T, norm):
+    """Post of seam k fused with the delayed pre of seam k+1: every token against the
+    oracle's composition (single-precision post, then the delayed pre on its bits)."""
+    d, y, post, comb = fused_case(T, 1100 + T, norm)
+    say("mhc_post_pre_delayed T=%d norm=%s" % (T, norm))
+    check_fused(run_fused(d, y, post, comb), d, y, post, comb, what="fused T=%d" % T)
+
+
+@pytest.mark.parametrize("T", [5, 300])
+def test_post_pre_delayed_equals_two_calls(T):
+    """The fused form gives the bits of mhc_post followed by mhc_pre_delayed for the
+    residual and layer_input; the gates agree to the bar (the projection's partial
+    sums are added in another order)."""
+    torch = torch_mod()
+    d, y, post, comb = fused_case(T, 1200 + T, True)
+    a = run_fused(d, y, post, comb)
+    xo = M.mhc_post(dev_bf16(y), dev_bf16(d["x"]), dev_f32(post), dev_f32(comb))
+    pre_out, po, co, li = M.mhc_pre_delayed(xo, dev_f32(d["pre_in"]), weights(d), dev_bf16(d["norm_weight"]),
+                                            d["eps"], d["iters"])
+    torch.cuda.synchronize()
+    say("fused vs two calls T=%d" % T)
+    assert np.array_equal(a[0], host_bits(xo))
+    check_gates(a[1], a[2], a[3], host_f32(pre_out), host_f32(po), host_f32(co), "fused vs two calls")
+    assert np.array_equal(a[4], host_bits(li))
