@@ -167,7 +167,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   if (any_alias(outs, 6, ins, 9)) return MHC_ERR_ALIAS;
 
   if (T == 0) return MHC_OK;
-  Plan pl = make_plan(T, KB, mode == kModeDelayed && C == kGroupC);
+  Plan pl = make_plan(T, KB, delayed && C == kGroupC);
   const size_t need = plan_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return MHC_ERR_WORKSPACE;
 
@@ -205,7 +205,10 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   if (pl.persist) {
     const int ng = persist_groups(T);
     if (ng > 0) {
-      hipLaunchKernelGGL(mhc_pre_persist_kernel<kGroupC>, dim3(ng * kPG), block, 0, s, p, ng);
+      if (fused)
+        hipLaunchKernelGGL((mhc_pre_persist_kernel<kGroupC, true>), dim3(ng * kPG), block, 0, s, p, ng);
+      else
+        hipLaunchKernelGGL((mhc_pre_persist_kernel<kGroupC, false>), dim3(ng * kPG), block, 0, s, p, ng);
       return launched();
     }
     // a device too small for one group: the split form (its workspace need is covered)

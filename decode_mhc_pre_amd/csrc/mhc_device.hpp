@@ -39,6 +39,11 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Component t (compile-time) of a uint4, as a float.
+__device__ __forceinline__ float u4_comp(const uint4& v, int t) {
+  return __uint_as_float(t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w);
+}
+
 __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
   f[0] = bf_even(v.x); f[1] = bf_odd(v.x);
   f[2] = bf_even(v.y); f[3] = bf_odd(v.y);

@@ -643,7 +643,7 @@ struct TokenGates {
   }
 };
 
-template <int kC>
+template <int kC, bool kFused>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   constexpr int kCBM = kC / kKB / kPG;   // 32-column blocks per member and stream
@@ -652,6 +652,10 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   constexpr int kUnit = 2 * kNS;         // loads covering two column blocks of all streams
   constexpr int kFragRows = kLd * kFragPerKB;
   constexpr int kNW = kThreads / kWave;
+  constexpr int kUnits = kCBM / 2;       // column-block pairs per member and tile
+  // fused: the first raw load issued after a tile's record stores (step 1) is
+  // the next unit's, consumed at step kUnit
+  constexpr int kArrive = kFused ? kUnit : kPArrive;
   static_assert(kC % (kKB * kPG) == 0 && kCBM % 2 == 0, "hidden size must split into column-block pairs");
   static_assert(kLd == 40 && kLd % kPQ == 0, "the exchange schedule assumes 40 loads per tile");
   static_assert(kNW * kTileT == kPT, "one 16-token MFMA tile per wave");
@@ -686,6 +690,13 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   };
   auto pin_rsrc = [&](int t) { return make_rsrc(p.pre_in + (size_t)max(t, 0) * kPT * kNS, tile_rows(t) * 16); };
   auto li_rsrc = [&](int t) { return make_rsrc(p.li + (size_t)max(t, 0) * kPT * kC, tile_rows(t) * kC * 2); };
+  // fused: sublayer output, next residual, the previous seam's post gates and comb
+  auto y_rsrc = [&](int t) { return make_rsrc(p.ysub + (size_t)max(t, 0) * kPT * kC, tile_rows(t) * kC * 2); };
+  auto xo_rsrc = [&](int t) {
+    return make_rsrc(p.xout + (size_t)max(t, 0) * kPT * (kNS * kC), tile_rows(t) * kRow);
+  };
+  auto gp_rsrc = [&](int t) { return make_rsrc(p.post_in + (size_t)max(t, 0) * kPT * kNS, tile_rows(t) * 16); };
+  auto gc_rsrc = [&](int t) { return make_rsrc(p.comb_in + (size_t)max(t, 0) * kPT * 16, tile_rows(t) * 64); };
   const int xsoff = cb0 * kKB * 2;   // byte offset of this member's first column (SGPR)
   int xls[kNS];                      // lane offset of each stream; the block offset fits the immediate
 #pragma unroll
@@ -697,6 +708,11 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
     const int u = n / kUnit, q = n % kUnit;
     const int s = q >> 1, cb = 2 * u + (q & 1);
     return buf_load16(r, xls[s] + cb * kKB * 2, xsoff);
+  };
+  // fused: raw load `kind` of column block cb: 0 the sublayer output, 1 + s stream s
+  auto raw_load = [&](rsrc_t rxx, rsrc_t ryy, int kind, int cb) {
+    return kind == 0 ? buf_load16(ryy, llane + cb * kKB * 2, xsoff)
+                     : buf_load16(rxx, xls[kind - 1] + cb * kKB * 2, xsoff);
   };
 
   unsigned* cnt_base = p.cnt + kPCntBase + (grp * kNW + wave) * kPSlots * kPCntStride;
@@ -710,9 +726,22 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
 
   // ---- prologue: first x loads and pre_in, then the weight slice into LDS
   rsrc_t rx = x_rsrc(tile_of(0));
+  rsrc_t ry = y_rsrc(tile_of(0));
   uint4 xq[kPQ];
+  uint4 rq[5][2];   // fused: one unit's raw loads [sublayer output, streams 0..3][block of the pair]
+  uint4 gq[5];      // fused: the lane token's post gates, then its comb rows 0..3
+  if constexpr (kFused) {
 #pragma unroll
-  for (int d = 0; d < kPQ; ++d) xq[d] = x_load(rx, d);
+    for (int kind = 0; kind < 5; ++kind)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) rq[kind][h] = raw_load(rx, ry, kind, h);
+    gq[0] = buf_load16(gp_rsrc(tile_of(0)), plane, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gq[1 + j] = buf_load16(gc_rsrc(tile_of(0)), plane * 4 + 16 * j, 0);
+  } else {
+#pragma unroll
+    for (int d = 0; d < kPQ; ++d) xq[d] = x_load(rx, d);
+  }
   uint4 pq = buf_load16(pin_rsrc(tile_of(0)), plane, 0);
   for (int r0 = 0; r0 < kFragRows; r0 += kNW * 10) {
     uint4 v[10];
@@ -735,13 +764,15 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   if (tid >= 32 && tid < 35) s_ba[kNL + tid - 32] = p.alpha[tid - 32];
   __syncthreads();
 
-  float y0[kCBM][8];                // the current tile's collapsed rows
+  float y0[kCBM][8];                // the current tile's collapsed rows (fused: parked as well)
   float y1[kCBM][8], y2[kCBM][8];   // parked in AGPRs: the previous two tiles'
+  float yw[2][8];                   // fused: the current unit's two blocks while they accumulate
+  uint4 xp[kNS][2];                 // fused: the current unit's next-residual fragments
 #pragma unroll
   for (int c = 0; c < kCBM; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      y0[c][e] = 0.f;
+      y0[c][e] = kFused ? agpr_park(0.f) : 0.f;
       y1[c][e] = y2[c][e] = agpr_park(0.f);
     }
   f32x4 pa0 = {0.f, 0.f, 0.f, 0.f}, pa1 = pa0, pa2 = pa0, pas = pa0;   // the last tile's accumulators
@@ -894,6 +925,8 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
     __asm__ volatile("" : "+v"(xls[0]), "+v"(xls[1]), "+v"(xls[2]), "+v"(xls[3]), "+v"(fb0), "+v"(fb1));
     const int tnext = tile_of(k + 1);
     const rsrc_t rxn = x_rsrc(tnext);
+    const rsrc_t ryn = y_rsrc(tnext);
+    const rsrc_t rxo = xo_rsrc(tile_of(k));
     const float p0 = __uint_as_float(pq.x), p1 = __uint_as_float(pq.y);
     const float p2 = __uint_as_float(pq.z), p3 = __uint_as_float(pq.w);
     unsigned* cnt1 = cnt_of(k - 1);
@@ -911,9 +944,26 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
       // first in the step so that it overlaps the wait for this step's x
       if (n < kPGateEnd || n >= kPIter) gt.step(p.iters);
       if (n == kPGateEnd) gt.finish(p);
-      const uint4 xv = xq[n % kPQ];
       const int u = n / kUnit, q = n % kUnit;
       const int s = q >> 1, cb = 2 * u + (q & 1);
+      if constexpr (kFused) {
+        if (q < 2) {
+          // the post stage for block cb: its four next-residual fragments, written out
+          float yf[8], a0[8], a1[8], a2[8], a3[8];
+          unpack8(rq[0][q], yf);
+          unpack8(rq[1][q], a0);
+          unpack8(rq[2][q], a1);
+          unpack8(rq[3][q], a2);
+          unpack8(rq[4][q], a3);
+#pragma unroll
+          for (int t = 0; t < kNS; ++t) {
+            xp[t][q] = post_stream8(u4_comp(gq[0], t), u4_comp(gq[1 + t], 0), u4_comp(gq[1 + t], 1),
+                                    u4_comp(gq[1 + t], 2), u4_comp(gq[1 + t], 3), yf, a0, a1, a2, a3);
+            buf_store16(xp[t][q], rxo, xls[t] + cb * kKB * 2, xsoff);
+          }
+        }
+      }
+      const uint4 xv = kFused ? xp[s][q & 1] : xq[n % kPQ];
       a0 = mfma_bf16(xv, fq[0], a0);
       a1 = mfma_bf16(xv, fq[1], a1);
       a2 = mfma_bf16(xv, fq[2], a2);
@@ -923,7 +973,26 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
       float f[8];
       unpack8(xv, f);
       const float ps = s == 0 ? p0 : s == 1 ? p1 : s == 2 ? p2 : p3;
-      if (s == 0) {
+      if constexpr (kFused) {
+        // all three row buffers are parked; the unit's two blocks accumulate in
+        // registers and are parked once complete
+        const int h = q & 1;
+        if (s == 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            y2[cb][e] = agpr_move(y1[cb][e]);
+            y1[cb][e] = agpr_move(y0[cb][e]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yw[h][e] = s == 0 ? ps * f[e] : yw[h][e] + ps * f[e];
+        if (s == kNS - 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(yw[h][e], yw[h][e], ssy);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y0[cb][e] = agpr_park(yw[h][e]);
+        }
+      } else if (s == 0) {
         // the buffers move down one place, block by block, just before this
         // tile's first write of the block: tile k-1's rows are parked, tile
         // k-2's rows move to the oldest buffer
@@ -933,26 +1002,28 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
           y1[cb][e] = agpr_park(ycur[cb][e]);
         }
       }
+      if constexpr (!kFused) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ycur[cb][e] = s == 0 ? ps * f[e] : ycur[cb][e] + ps * f[e];
-      if (s == kNS - 1) {
+        for (int e = 0; e < 8; ++e) ycur[cb][e] = s == 0 ? ps * f[e] : ycur[cb][e] + ps * f[e];
+        if (s == kNS - 1) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(ycur[cb][e], ycur[cb][e], ssy);
-      }
-      // refill: this tile's load n + kPQ, or the next tile's first loads
-      const int m = n + kPQ;
-      if (m < kLd) {
-        xq[n % kPQ] = x_load(rx, m);
-      } else {
-        xq[n % kPQ] = x_load(rxn, m - kLd);
-        if (m == kLd) pq = buf_load16(pin_rsrc(tnext), plane, 0);
+          for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(ycur[cb][e], ycur[cb][e], ssy);
+        }
+        // refill: this tile's load n + kPQ, or the next tile's first loads
+        const int m = n + kPQ;
+        if (m < kLd) {
+          xq[n % kPQ] = x_load(rx, m);
+        } else {
+          xq[n % kPQ] = x_load(rxn, m - kLd);
+          if (m == kLd) pq = buf_load16(pin_rsrc(tnext), plane, 0);
+        }
       }
       // ---- exchange of tile k-1
       if (n == kPPubA) publish_a();
       if (n == kPPubB) publish_b(k - 1);
-      if (n == kPArrive) {
-        // xv is the first x load issued after tile k-1's records were stored
-        const unsigned z = zero_after(xv.x);
+      if (n == kArrive) {
+        // the first x load issued after tile k-1's records were stored has returned
+        const unsigned z = zero_after(kFused ? rq[0][0].x : xv.x);
         if (lane == 0) __hip_atomic_fetch_add(cnt1, 1u + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       // ---- exchange of tile k-2 and its layer_input
@@ -980,8 +1051,32 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
         for (int c = 0; c < kCBM; ++c)
           if (n == kLiStep[c]) li_store(y2[c], true, ry2, rl2, c);
       }
+      // fused refill, once the unit's raw loads are consumed (and after this
+      // step's record stores): the next unit, or the next tile's first unit
+      // with its pre_in and gates
+      if constexpr (kFused) {
+        if (q == 1) {
+          __asm__ volatile("" ::: "memory");
+          if (u + 1 < kUnits) {
+#pragma unroll
+            for (int kind = 0; kind < 5; ++kind)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) rq[kind][h] = raw_load(rx, ry, kind, 2 * (u + 1) + h);
+          } else {
+#pragma unroll
+            for (int kind = 0; kind < 5; ++kind)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) rq[kind][h] = raw_load(rxn, ryn, kind, h);
+            pq = buf_load16(pin_rsrc(tnext), plane, 0);
+            gq[0] = buf_load16(gp_rsrc(tnext), plane, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gq[1 + j] = buf_load16(gc_rsrc(tnext), plane * 4 + 16 * j, 0);
+          }
+        }
+      }
     }
     rx = rxn;
+    ry = ryn;
 
     pa0 = a0;
     pa1 = a1;
@@ -1019,7 +1114,7 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   wait_vmem();   // tile kl's records are stored
   if (lane == 0) __hip_atomic_fetch_add(cnt_of(kl), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (kl >= 1) finish_tile(kl - 1, y1, true);
-  finish_tile(kl, y0, false);
+  finish_tile(kl, y0, kFused);
 
   // ---- the last wave of the grid to finish resets the counters
   wait_vmem();

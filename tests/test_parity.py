@@ -384,7 +384,7 @@ def test_post_pre_delayed(T, norm):
     check_fused(run_fused(d, y, post, comb), d, y, post, comb, what="fused T=%d" % T)
 
 
-@pytest.mark.parametrize("T", [5, 300])
+@pytest.mark.parametrize("T", [5, 300, 4100])
 def test_post_pre_delayed_equals_two_calls(T):
     """The fused form gives the bits of mhc_post followed by mhc_pre_delayed for the
     residual and layer_input; the gates agree to the bar (the projection's partial
@@ -400,3 +400,40 @@ def test_post_pre_delayed_equals_two_calls(T):
     assert np.array_equal(a[0], host_bits(xo))
     check_gates(a[1], a[2], a[3], host_f32(pre_out), host_f32(po), host_f32(co), "fused vs two calls")
     assert np.array_equal(a[4], host_bits(li))
+
+
+@pytest.mark.parametrize("T", [2048, 2113, 3999])
+def test_persistent_fused_every_token(T):
+    """Token counts served by the persistent fused kernel (the persistent delayed
+    kernel with the post stage in front), every token against the oracle
+    composition, with the norm and without it."""
+    for norm in (True, False):
+        d, y, post, comb = fused_case(T, 1300 + T, norm, outlier_frac=0.01)
+        say("persistent fused T=%d norm=%s" % (T, norm))
+        check_fused(run_fused(d, y, post, comb), d, y, post, comb, what="persist fused T=%d" % T)
+
+
+def test_persistent_fused_repeat_and_workspace_reset():
+    """Back-to-back fused calls of different sizes on one workspace repeat bit for
+    bit, and the counters are back at zero."""
+    torch = torch_mod()
+    cs = {T: fused_case(T, 1400 + T, True) for T in (4096, 2048)}
+    first = {T: run_fused(*cs[T]) for T in (4096, 2048)}
+    for T in (2048, 4096, 2048):
+        again = run_fused(*cs[T])
+        for u, v in zip(first[T], again):
+            assert np.array_equal(u, v)
+    ws = M.workspace(torch.device("cuda"), 4096, C)
+    assert int(ws[:4096].view(torch.int32).abs().sum()) == 0
+
+
+def test_fused_seam_prefill_sampled():
+    """T = 16384, the prefill seam fused: post of seam k (configuration 3's shapes)
+    into the delayed pre of seam k+1 with the norm and 1% outlier rows (configuration
+    2's); GPU on all tokens in the benchmark's launch, oracle on sampled rows."""
+    T = 16384
+    d, y, post, comb = fused_case(T, 2, True, outlier_frac=0.01)
+    rows = _sample_rows(T, d["outliers"])
+    got = run_fused(d, y, post, comb, rows)
+    say("fused prefill sampled rows: %d" % len(rows))
+    check_fused(got, d, y, post, comb, rows=rows, what="fused T=16384")
