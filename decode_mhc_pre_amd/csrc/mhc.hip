@@ -47,16 +47,28 @@ Plan make_plan(int T, int KB, bool persist_ok) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace layout.
-//   split form:      counters [ntile] u32 (padded to 256 B), partials [ntile][nsplit][16][25] f32
-//   persistent form: word 0 finished waves, word 2 wait-budget flag, arrival counters
-//                    [group][wave][5] 256 B apart from word 64; records [group][wave][4]
-//                    (1 KB sum-y^2 block + 32 KB value block) from 128 KiB
-size_t counter_bytes(const Plan& pl) { return align_up((size_t)pl.ntile * sizeof(unsigned), 256); }
+// Workspace layout.  Counters must read zero when a call starts, and one
+// workspace serves calls of both forms, so the two forms' counters live in
+// disjoint places that nothing else writes; their data (rewritten before it is
+// read in every call) share the region from 128 KiB.
+//   [0, 256)            persistent form: word 0 finished waves, word 2 wait-budget flag
+//   [256, 82176)        persistent form: arrival counters [group][wave][5], 256 B apart
+//   [96 KiB, +512)      split form: tile counters [ntile] u32 (ntile < 128 whenever split)
+//   [128 KiB, ...)      split form: partials [ntile][nsplit][16][25] f32, or
+//                       persistent form: records [group][wave][4] (1 KB + 32 KB each)
+constexpr size_t kSplitCntOffset = 96 * 1024;
+static_assert(kSplitCntOffset + kTargetProjGroups * sizeof(unsigned) <= kPPartOffset,
+              "split counters overlap the data region");
+static_assert(kPCntBase * 4 + (size_t)kPMaxGroups * 4 * kPSlots * kPCntStride * 4 <= kSplitCntOffset,
+              "persistent counters overlap the split counters");
 size_t plan_ws_bytes(const Plan& pl) {
   if (pl.persist) return persist_ws_bytes();
   if (pl.nsplit <= 1) return 0;
-  return counter_bytes(pl) + (size_t)pl.ntile * pl.nsplit * kTileT * kPartStride * sizeof(float);
+  return kPPartOffset + (size_t)pl.ntile * pl.nsplit * kTileT * kPartStride * sizeof(float);
+}
+void set_split_ws(PreParams& p, void* ws) {
+  p.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kSplitCntOffset);
+  p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + kPPartOffset);
 }
 
 // Groups of the persistent kernel: one workgroup per CU at most (its LDS use
@@ -186,10 +198,14 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   p.ysub = pi.y;
   p.post_in = pi.post;
   p.comb_in = pi.comb;
-  p.cnt = need ? static_cast<unsigned*>(ws) : nullptr;
-  p.part = need ? reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                           (pl.persist ? kPPartOffset : counter_bytes(pl)))
-                : nullptr;
+  p.cnt = nullptr;
+  p.part = nullptr;
+  if (need && pl.persist) {
+    p.cnt = static_cast<unsigned*>(ws);
+    p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + kPPartOffset);
+  } else if (need) {
+    set_split_ws(p, ws);
+  }
   p.eps = eps;
   p.iters = iters;
   p.T = T;
@@ -216,9 +232,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
     p.ntile = pl.ntile;
     p.nsplit = pl.nsplit;
     p.nproj = pl.nproj;
-    if (pl.nsplit > 1) {
-      p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(pl));
-    }
+    if (pl.nsplit > 1) set_split_ws(p, ws);
   }
   switch (mode) {
     case kModePre:

@@ -137,8 +137,9 @@ mhc_status mhc_post(const uint16_t *y, const uint16_t *x, const float *post,
  * launches per seam; the delayed form makes it possible because the pre-mix
  * that collapses seam k+1 is seam k's, known before the pass).  The results
  * are those of mhc_post(y, x, post_in, comb_in) -> x_out followed by
- * mhc_pre_delayed(x_out, pre_in, ...): x_out and layer_input bit for bit, the
- * gates up to the order in which the projection's partial sums are added:
+ * mhc_pre_delayed(x_out, pre_in, ...): x_out bit for bit, layer_input without
+ * the norm bit for bit; the gates, and the norm factor, up to the order in
+ * which partial sums are added:
  *   y        [T][C] bf16      sublayer output of seam k.
  *   x        [T][n][C] bf16   residual entering seam k.
  *   post_in  [T][n] float     seam k's post gates; comb_in [T][n][n] float its comb.

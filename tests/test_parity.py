@@ -11,7 +11,7 @@ import decode_mhc_pre_amd as M
 import mhc_inputs as mi
 import oracle
 from gpu_util import (check_bf16, check_gates, dev_bf16, dev_f32, host_bits, host_f32,
-                      rms_over_weight, say, torch_mod)
+                      rms_over_weight, say, torch_mod, ulp_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -285,7 +285,7 @@ def test_persistent_repeat_and_workspace_reset():
         for u, v in zip(first[T], again):
             assert np.array_equal(u, v)
     ws = M.workspace(torch.device("cuda"), 4096, C)
-    assert int(ws[:4096].view(torch.int32).abs().sum()) == 0
+    assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
 
 
 @pytest.mark.parametrize("T", [1, 7, 300])
@@ -325,6 +325,10 @@ def test_config3_post_sampled():
     check_bf16(ob, o["out_val"], o["out_mag"], what="cfg3 out")
 
 
+# every counter of both kernel forms lies in the workspace's first 128 KiB
+COUNTER_BYTES = 128 * 1024
+
+
 def test_repeatable_and_workspace_reset():
     """Split-K runs leave the workspace counters at zero: back-to-back calls on
     one workspace, with different token counts, give identical bits."""
@@ -336,8 +340,7 @@ def test_repeatable_and_workspace_reset():
         for u, v in zip(a, b):
             assert np.array_equal(u, v)
     ws = M.workspace(torch.device("cuda"), 1, C)
-    n_cnt = 256
-    assert int(ws[: 4 * n_cnt].view(torch.int32).abs().sum()) == 0
+    assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
 
 
 # ----------------------------------------------------------------------------- post -> delayed pre, fused
@@ -386,20 +389,26 @@ def test_post_pre_delayed(T, norm):
 
 @pytest.mark.parametrize("T", [5, 300, 4100])
 def test_post_pre_delayed_equals_two_calls(T):
-    """The fused form gives the bits of mhc_post followed by mhc_pre_delayed for the
-    residual and layer_input; the gates agree to the bar (the projection's partial
-    sums are added in another order)."""
+    """The fused form against mhc_post followed by mhc_pre_delayed: the residual bit
+    for bit, layer_input without the norm bit for bit; the gates, and layer_input
+    with the norm, to the bar (partial sums are added in another order)."""
     torch = torch_mod()
-    d, y, post, comb = fused_case(T, 1200 + T, True)
-    a = run_fused(d, y, post, comb)
-    xo = M.mhc_post(dev_bf16(y), dev_bf16(d["x"]), dev_f32(post), dev_f32(comb))
-    pre_out, po, co, li = M.mhc_pre_delayed(xo, dev_f32(d["pre_in"]), weights(d), dev_bf16(d["norm_weight"]),
-                                            d["eps"], d["iters"])
-    torch.cuda.synchronize()
-    say("fused vs two calls T=%d" % T)
-    assert np.array_equal(a[0], host_bits(xo))
-    check_gates(a[1], a[2], a[3], host_f32(pre_out), host_f32(po), host_f32(co), "fused vs two calls")
-    assert np.array_equal(a[4], host_bits(li))
+    for norm in (False, True):
+        d, y, post, comb = fused_case(T, 1200 + T, norm)
+        nw = dev_bf16(d["norm_weight"]) if norm else None
+        a = run_fused(d, y, post, comb)
+        xo = M.mhc_post(dev_bf16(y), dev_bf16(d["x"]), dev_f32(post), dev_f32(comb))
+        pre_out, po, co, li = M.mhc_pre_delayed(xo, dev_f32(d["pre_in"]), weights(d), nw, d["eps"], d["iters"])
+        torch.cuda.synchronize()
+        say("fused vs two calls T=%d norm=%s" % (T, norm))
+        assert np.array_equal(a[0], host_bits(xo))
+        check_gates(a[1], a[2], a[3], host_f32(pre_out), host_f32(po), host_f32(co), "fused vs two calls")
+        lb = host_bits(li)
+        if norm:
+            va, vb = oracle.bf16_to_f64(a[4]), oracle.bf16_to_f64(lb)
+            assert np.all(np.abs(va - vb) <= ulp_bf16(np.maximum(np.abs(va), np.abs(vb))))
+        else:
+            assert np.array_equal(a[4], lb)
 
 
 @pytest.mark.parametrize("T", [2048, 2113, 3999])
@@ -424,7 +433,7 @@ def test_persistent_fused_repeat_and_workspace_reset():
         for u, v in zip(first[T], again):
             assert np.array_equal(u, v)
     ws = M.workspace(torch.device("cuda"), 4096, C)
-    assert int(ws[:4096].view(torch.int32).abs().sum()) == 0
+    assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
 
 
 def test_fused_seam_prefill_sampled():
@@ -437,3 +446,29 @@ def test_fused_seam_prefill_sampled():
     got = run_fused(d, y, post, comb, rows)
     say("fused prefill sampled rows: %d" % len(rows))
     check_fused(got, d, y, post, comb, rows=rows, what="fused T=16384")
+
+
+def test_workspace_shared_by_split_and_persistent_forms():
+    """One workspace serves both kernel forms: a split call (partial sums in the
+    workspace) followed by persistent calls, and the reverse, stay correct, and
+    every counter is back at zero after each call."""
+    torch = torch_mod()
+    ws = M.workspace(torch.device("cuda"), 4100, C)
+    small = mi.pre_inputs(300, seed=1500, delayed=True, norm=True)
+    big = fused_case(4100, 1501, True)
+    for rnd in range(2):
+        say("shared workspace round %d: split T=300" % rnd)
+        pre_out, post, comb, li = run_delayed(small)
+        o = oracle_delayed(small)
+        check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "split after persistent")
+        assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
+        say("shared workspace round %d: persistent fused T=4100" % rnd)
+        check_fused(run_fused(*big), *big, what="persistent fused after split")
+        assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
+        run_delayed(small)
+        say("shared workspace round %d: persistent delayed T=4100" % rnd)
+        d = big[0]
+        pre_out, post, comb, li = run_delayed(d)
+        o = oracle_delayed(d)
+        check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "persistent after split")
+        assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
