@@ -1,13 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the mHC seam block on one MI355X.
 
-A step is one pass of the seam's hot path over one batch of T = 16384 tokens
-(n = 4 streams, hidden C = 5120, fused RMSNorm, 20 Sinkhorn iterations):
-    mhc_pre_delayed(x, pre_in) -> pre_out, post, comb, layer_input
-    mhc_post(y' = layer_input, x, post, comb) -> next residual
-(the sublayer between them is the identity stand-in; attention / MoE are not
-part of the seam).  Inputs are synthetic, seeded, and resident in HBM before
-the timed region.  Prints one JSON line.
+A step is one seam of the hot path over one batch of T = 16384 tokens (n = 4
+streams, hidden C = 5120, fused RMSNorm, 20 Sinkhorn iterations): the post
+stage of seam k and the delayed pre stage of seam k+1, in one launch,
+    mhc_post_pre_delayed(y, x, post_k, comb_k, pre_k) -> x', pre, post, comb, layer_input
+(one post and one pre per token and step, as in a decoder's steady state; the
+sublayer output y is synthetic, attention / MoE are not part of the seam).
+The same seam as two launches (mhc_post, then mhc_pre_delayed on its output) is
+timed beside it.  Inputs are synthetic, seeded, and resident in HBM before the
+timed region.  Prints one JSON line.
 
 Also reported: per-kernel durations from HIP events on the launch stream, the
 roofline of the dominant kernel, a microseconds-per-call sweep at T = 1..128
@@ -47,6 +49,15 @@ def pre_bytes(T, C=C, norm=True, delayed=True):
 def post_bytes(T, C=C):
     """Algorithmic HBM bytes of one post call: y, x, out, post, comb."""
     return T * (C * 2 + 2 * NS * C * 2 + 16 + 64)
+
+
+def fused_bytes(T, C=C, norm=True):
+    """Algorithmic HBM bytes of one fused seam: y, x and the previous gates and pre-mix in;
+    the next residual, layer_input and this seam's gates out; weights once."""
+    K = NS * C
+    per_tok = C * 2 + K * 2 + (16 + 64 + 16) + K * 2 + C * 2 + (16 + 16 + 64)
+    fixed = K * 24 * 4 + 24 * 4 + 3 * 4 + (C * 2 if norm else 0)
+    return T * per_tok + fixed
 
 
 def entry_bytes(T, C=C, norm=True):
@@ -131,57 +142,89 @@ def main():
     pre_in_host_sample = d["pre_in"][:4096].copy()
     fn_h, bias_h, alpha_h, nw_h = d["fn"], d["bias"], d["alpha"], d["norm_weight"]
     del d
+    # seam k's sublayer output and gates: y ~ N(0,1) bf16, gates from the library's own
+    # pre stage on the same residual (real gates: post in (0,2), comb column-stochastic)
+    y_h = mi.post_inputs(T_SEAM, seed=3)["y"]
+    y = bf(y_h)
+    y_host_sample = y_h[:4096].copy()
+    del y_h
     pre_out, post, comb, li = M._pre_outputs(T_SEAM, C, dev)
-    out = torch.empty_like(x)
     ws = M.workspace(dev, T_SEAM, C)
+    pre_k, post_k, comb_k, _ = M.mhc_pre_delayed(x, pre_in, w, nw, 1e-6, 20, ws=ws)
+    x_next = torch.empty_like(x)
     torch.cuda.synchronize()
+    post_k_h, comb_k_h, pre_k_h = (post_k[:4096].cpu().numpy(), comb_k[:4096].cpu().numpy(),
+                                   pre_k[:4096].cpu().numpy())
     print("inputs ready in %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
+        # post of seam k and delayed pre of seam k+1, one launch
         if ev is not None:
             ev[0].record(stream)
-        M.mhc_pre_delayed(x, pre_in, w, nw, 1e-6, 20, out=(pre_out, post, comb, li), ws=ws)
+        M.mhc_post_pre_delayed(y, x, post_k, comb_k, pre_k, w, nw, 1e-6, 20,
+                               out=(x_next, pre_out, post, comb, li), ws=ws)
         if ev is not None:
             ev[1].record(stream)
-        M.mhc_post(li, x, post, comb, out=out)
+
+    def step_two(ev=None):
+        # the same seam as two launches
+        if ev is not None:
+            ev[0].record(stream)
+        M.mhc_post(y, x, post_k, comb_k, out=x_next)
+        if ev is not None:
+            ev[1].record(stream)
+        M.mhc_pre_delayed(x_next, pre_k, w, nw, 1e-6, 20, out=(pre_out, post, comb, li), ws=ws)
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def timed(fn, nev):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for k in range(args.steps):
+            fn(evs[k])
+        torch.cuda.synchronize()
+        return time.perf_counter() - t_start, evs
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
-    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    post_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    t_total, evs = timed(step, 2)
+    fused_ms = [e[0].elapsed_time(e[1]) for e in evs]
     ms_per_step = t_total * 1e3 / args.steps
     value = T_SEAM * args.steps / t_total
+    t_two, evs2 = timed(step_two, 3)
+    post_ms = [e[0].elapsed_time(e[1]) for e in evs2]
+    pre_ms = [e[1].elapsed_time(e[2]) for e in evs2]
 
+    fused_avg = sum(fused_ms) / len(fused_ms)
     pre_avg = sum(pre_ms) / len(pre_ms)
     post_avg = sum(post_ms) / len(post_ms)
-    pb, qb = pre_bytes(T_SEAM), post_bytes(T_SEAM)
+    fb, pb, qb = fused_bytes(T_SEAM), pre_bytes(T_SEAM), post_bytes(T_SEAM)
+
+    def kentry(avg_ms, nbytes, key):
+        return dict(avg_us=avg_ms * 1e3, alg_bytes=nbytes, gbs=nbytes / (avg_ms * 1e-3) / 1e9,
+                    traffic=measured_traffic(key))
+
     kernels = {
-        "mhc_pre_persist_kernel": dict(avg_us=pre_avg * 1e3, alg_bytes=pb, gbs=pb / (pre_avg * 1e-3) / 1e9,
-                                     traffic=measured_traffic("mhc_pre_persist_kernel")),
-        "mhc_post_kernel": dict(avg_us=post_avg * 1e3, alg_bytes=qb, gbs=qb / (post_avg * 1e-3) / 1e9,
-                                traffic=measured_traffic("mhc_post_kernel")),
+        "mhc_pre_persist_kernel<5120, true>": kentry(fused_avg, fb, "mhc_pre_persist_kernel<5120, true>"),
+        "mhc_pre_persist_kernel<5120, false>": kentry(pre_avg, pb, "mhc_pre_persist_kernel<5120, false>"),
+        "mhc_post_kernel": kentry(post_avg, qb, "mhc_post_kernel"),
     }
     for v in kernels.values():
         v["frac"] = v["gbs"] / HBM_PEAK_GBS
-    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    # the timed step is the fused kernel alone
+    dom = "mhc_pre_persist_kernel<5120, true>"
     traffic = kernels[dom]["traffic"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(kernels[dom]["gbs"], 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kernels[dom]["frac"], 4),
                 "traffic": traffic}
-    seam_gbs = (pb + qb) / (t_total / args.steps) / 1e9
+    seam_gbs = fb / (t_total / args.steps) / 1e9
+    two_call = {"tokens_per_s": round(T_SEAM * args.steps / t_two, 1),
+                "ms_per_step": round(t_two * 1e3 / args.steps, 4),
+                "alg_GBps": round((pb + qb) / (t_two / args.steps) / 1e9, 1), "launches_per_seam": 2}
 
     if args.copy_ref:
         # a plain copy kernel of known size: reads and writes 512 MiB each
@@ -198,14 +241,14 @@ def main():
         sweep = run_sweep(torch, M, mi, dev, bf, f32, w, nw)
     entry = None if args.no_sweep else run_entry(torch, M, mi, dev, bf, f32)
 
-    del x, out, li
+    del x, x_next, li, y
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(x_host_sample, pre_in_host_sample, fn_h, bias_h, alpha_h, nw_h,
-                           args.cpu_seconds)
+        cpu = cpu_baseline(y_host_sample, x_host_sample, post_k_h, comb_k_h, pre_k_h, fn_h, bias_h, alpha_h,
+                           nw_h, args.cpu_seconds)
 
     line = {
         "metric": METRIC,
@@ -220,8 +263,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "mhc seam: pre_delayed + fused RMSNorm + post, T=16384, n=4, C=5120, "
-                               "20 Sinkhorn iters, 1% outlier rows x100",
+        "config": {"workload": "mhc seam, one launch: post of seam k + delayed pre of seam k+1 with "
+                               "fused RMSNorm, T=16384, n=4, C=5120, 20 Sinkhorn iters, 1% outlier rows x100",
                    "T": T_SEAM, "hc_mult": NS, "hidden": C, "sinkhorn_iters": 20,
                    "parallelism": "single GPU"},
         "roofline": roofline,
@@ -229,7 +272,8 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "seam_alg_GBps": round(seam_gbs, 1),
-        "launches_per_seam": 2,
+        "launches_per_seam": 1,
+        "two_call_seam": two_call,
         "us_per_call_sweep": sweep,
         "entry": entry,
     }
@@ -270,8 +314,15 @@ def run_sweep(torch, M, mi, dev, bf, f32, w, nw):
             pre_call()
             post_call()
 
+        fo = (torch.empty_like(x),) + tuple(M._pre_outputs(T, C, dev))
+
+        def fused_call():
+            # post of the previous seam (gates: this seam's outputs above) and the delayed pre
+            M.mhc_post_pre_delayed(outs[3], x, outs[1], outs[2], pin, w, nw, 1e-6, 20, out=fo, ws=ws)
+
         row = {}
-        for name, fn in (("pre_delayed", pre_call), ("post", post_call), ("seam", seam_call)):
+        for name, fn in (("pre_delayed", pre_call), ("post", post_call), ("seam", seam_call),
+                         ("seam_fused", fused_call)):
             fn()
             torch.cuda.synchronize()
             # eager: host launch path included
@@ -311,19 +362,17 @@ def run_entry(torch, M, mi, dev, bf, f32):
     return res
 
 
-def cpu_baseline(x, pre_in, fn, bias, alpha, nw, target_s):
-    """The oracle as it stands (float64 C, OpenMP over tokens) on a bounded
-    sample of the same seam: pre_delayed with fused norm, then post."""
+def cpu_baseline(y, x, post_k, comb_k, pre_k, fn, bias, alpha, nw, target_s):
+    """The oracle as it stands (C, OpenMP over tokens) on a bounded sample of the
+    same seam: the post stage of seam k, then the delayed pre with fused norm."""
     import oracle
     oracle.lib()
     threads = oracle.max_threads()
 
     def run(S):
         t = time.perf_counter()
-        o = oracle.mhc_pre_delayed(x[:S], pre_in[:S], fn, bias, alpha, 1e-6, 20, norm_weight=nw)
-        post = o["post"].astype(np.float32)
-        comb = o["comb"].astype(np.float32)
-        oracle.mhc_post(o["li"], x[:S], post, comb)
+        oracle.mhc_post_pre_delayed(y[:S], x[:S], post_k[:S], comb_k[:S], pre_k[:S], fn, bias, alpha, 1e-6, 20,
+                                    norm_weight=nw)
         return time.perf_counter() - t
 
     S = min(len(x), 2048)
@@ -342,7 +391,7 @@ def cpu_baseline(x, pre_in, fn, bias, alpha, nw, target_s):
     except OSError:
         pass
     return {"value": round(S * reps / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d tokens of the T=16384 seam input (pre_delayed+norm then post) x %d passes, "
+            "sample": "%d tokens of the T=16384 seam input (post, then pre_delayed+norm) x %d passes, "
                       "%.1f s; %s" % (S, reps, dt, cpu_model)}
 
 
