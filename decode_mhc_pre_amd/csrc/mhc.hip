@@ -14,16 +14,31 @@ namespace {
 
 using namespace mhc;
 
-// Projection workgroups aimed for when few tokens: splitting the 4C row over
-// workgroups spreads the (L2/HBM-resident) projection weight over the chip.
-constexpr int kTargetProjGroups = 128;
-constexpr int kMinKBPerSplit = 8;  // two 32-k steps per wave at least
+// Few tokens: the 4C row of a 16-token tile is split over workgroups, which
+// spreads the (L2/HBM-resident) projection weight over the chip; the last
+// split to arrive sums the partials.  More splits shorten the weight reads and
+// lengthen that sum.  Measured on MI355X (delayed pre, C = 5120, graph replay),
+// the best split count per tile count: 16 splits for 1-2 tiles (T <= 32),
+// 8 for 3-4, 4 for 5-16, 2 for 17-32, none beyond (e.g. T = 1: 10.9 us with 16
+// splits vs 17.5 us with 80; T = 128: 20.8 vs 25.6 us with 16).
+constexpr int kMaxSplitTiles = 32;  // tiles beyond which the row is never split
+constexpr int kMinKBPerSplit = 8;   // two 32-k steps per wave at least
+int splits_for(int ntile) {
+  return ntile <= 2 ? 16 : ntile <= 4 ? 8 : ntile <= 16 ? 4 : ntile <= kMaxSplitTiles ? 2 : 1;
+}
 constexpr int kMaxC = 16384;
 // The persistent delayed kernel keeps a tile's collapsed rows on chip and
-// splits each 64-token tile over a group of 16 workgroups: worth it once the
-// groups fill the chip.
+// splits each 64-token tile over a group of 16 workgroups.  Measured against
+// the split form (graph replay, C = 5120): even at T = 256 (four groups) it
+// ties for the delayed pre (25.8 vs 25.4 us) and wins for the fused seam
+// (32.7 vs 43.9 us); from T = 512 on it wins both (30 vs 35, 37 vs 69 us).
 constexpr int kGroupC = 5120;
-constexpr int kGroupMinT = 2048;
+constexpr int kGroupMinT = 256;
+// Fused seam below kGroupMinT: the split kernel's fused mode is the fastest
+// form up to 8 tokens (T = 1: 12.4 us vs 13.7 us for two launches); from 16
+// tokens on, the post kernel followed by the delayed split kernel is (T = 16:
+// 15.4 vs 17.7 us; T = 128: 26.9 vs 39.7 us).
+constexpr int kFusedSplitMaxT = 8;
 
 struct Plan {
   int ntile, nsplit, nproj;
@@ -34,9 +49,7 @@ Plan make_plan(int T, int KB, bool persist_ok) {
   Plan pl;
   pl.ntile = (T + kTileT - 1) / kTileT;
   pl.persist = persist_ok && T >= kGroupMinT;
-  int ns = (pl.persist || pl.ntile >= kTargetProjGroups)
-               ? 1
-               : (kTargetProjGroups + pl.ntile - 1) / pl.ntile;
+  int ns = pl.persist ? 1 : splits_for(pl.ntile);
   int maxs = KB / kMinKBPerSplit;
   if (maxs < 1) maxs = 1;
   if (ns > maxs) ns = maxs;
@@ -53,11 +66,11 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // read in every call) share the region from 128 KiB.
 //   [0, 256)            persistent form: word 0 finished waves, word 2 wait-budget flag
 //   [256, 82176)        persistent form: arrival counters [group][wave][5], 256 B apart
-//   [96 KiB, +512)      split form: tile counters [ntile] u32 (ntile < 128 whenever split)
+//   [96 KiB, +128)      split form: tile counters [ntile] u32 (ntile <= 32 whenever split)
 //   [128 KiB, ...)      split form: partials [ntile][nsplit][16][25] f32, or
 //                       persistent form: records [group][wave][4] (1 KB + 32 KB each)
 constexpr size_t kSplitCntOffset = 96 * 1024;
-static_assert(kSplitCntOffset + kTargetProjGroups * sizeof(unsigned) <= kPPartOffset,
+static_assert(kSplitCntOffset + kMaxSplitTiles * sizeof(unsigned) <= kPPartOffset,
               "split counters overlap the data region");
 static_assert(kPCntBase * 4 + (size_t)kPMaxGroups * 4 * kPSlots * kPCntStride * 4 <= kSplitCntOffset,
               "persistent counters overlap the split counters");
@@ -218,6 +231,16 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 block(kThreads);
+  if (fused && !pl.persist && T > kFusedSplitMaxT) {
+    // two launches: the post stage writes x_out, the delayed pre reads it
+    const int C8 = C / 8;
+    const long long total = (long long)T * C8;
+    hipLaunchKernelGGL(mhc_post_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), block, 0, s,
+                       reinterpret_cast<const uint4*>(pi.y), reinterpret_cast<const uint4*>(x), pi.post,
+                       pi.comb, reinterpret_cast<uint4*>(x_out), T, C8);
+    p.x = x_out;
+    mode = kModeDelayed;
+  }
   if (pl.persist) {
     const int ng = persist_groups(T);
     if (ng > 0) {
@@ -280,7 +303,7 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
   const int KBs[2] = {C / kKB, MHC_HC_MULT * C / kKB};
   const int ntile_max = (T_max + kTileT - 1) / kTileT;
   for (int KB : KBs) {
-    for (int nt = 1; nt <= ntile_max && nt <= kTargetProjGroups; ++nt) {
+    for (int nt = 1; nt <= ntile_max && nt <= kMaxSplitTiles; ++nt) {
       const Plan pl = make_plan(nt * kTileT, KB, false);
       const size_t b = plan_ws_bytes(pl);
       if (b > best) best = b;

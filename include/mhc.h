@@ -151,9 +151,10 @@ mhc_status mhc_post(const uint16_t *y, const uint16_t *x, const float *post,
  *            rounded once (the same bits as mhc_post).
  *   pre_out, post, comb, layer_input: seam k+1's outputs, from x_out, as in
  *            mhc_pre_delayed.
- * The workspace is that of mhc_pre_delayed (mhc_workspace_bytes).  x_out must
- * not overlap x or any other argument: this form is not in place
- * (MHC_ERR_ALIAS). */
+ * Launches: one for T <= 8 and, with C = 5120, for T >= 256; in between the
+ * post kernel and then the delayed pre kernel (measured faster there).  The
+ * workspace is that of mhc_pre_delayed (mhc_workspace_bytes).  x_out must not
+ * overlap x or any other argument: this form is not in place (MHC_ERR_ALIAS). */
 mhc_status mhc_post_pre_delayed(const uint16_t *y, const uint16_t *x,
                                 const float *post_in, const float *comb_in,
                                 const float *pre_in, int T, int n, int C,

@@ -40,7 +40,8 @@ def test_sizes():
     assert m.mhc_workspace_bytes(1, 4, C) > 0
     # few tokens: split partials, bounded; many tokens (persistent delayed
     # form): a fixed set of exchange records, whatever the token count
-    assert m.mhc_workspace_bytes(1024, 4, C) < 2 * MiB
+    assert m.mhc_workspace_bytes(128, 4, C) < 2 * MiB
+    assert m.mhc_workspace_bytes(256, 4, C) == m.mhc_workspace_bytes(16384, 4, C)
     assert m.mhc_workspace_bytes(16384, 4, C) < 16 * MiB
     assert m.mhc_workspace_bytes(1 << 20, 4, C) == m.mhc_workspace_bytes(16384, 4, C)
     assert m.mhc_workspace_bytes(1 << 20, 4, 4096) < 2 * MiB   # no grouped form for C != 5120

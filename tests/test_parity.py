@@ -454,10 +454,10 @@ def test_workspace_shared_by_split_and_persistent_forms():
     every counter is back at zero after each call."""
     torch = torch_mod()
     ws = M.workspace(torch.device("cuda"), 4100, C)
-    small = mi.pre_inputs(300, seed=1500, delayed=True, norm=True)
+    small = mi.pre_inputs(100, seed=1500, delayed=True, norm=True)   # split form, 4 splits per tile
     big = fused_case(4100, 1501, True)
     for rnd in range(2):
-        say("shared workspace round %d: split T=300" % rnd)
+        say("shared workspace round %d: split T=100" % rnd)
         pre_out, post, comb, li = run_delayed(small)
         o = oracle_delayed(small)
         check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "split after persistent")
