@@ -194,6 +194,76 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
   }
 }
 
+// ------------------------------------------------------------------ collapse + norm, one token per wave
+// For the 16 tokens a projection workgroup has just gated (own pre-mix): with
+// hidden sizes up to 5120 a token's collapsed row fits one wave's registers (at
+// most 10 chunks of 8 per lane), so the four waves take a token each instead
+// of the whole workgroup taking the tokens one after another (measured at
+// T = 16384: mhc_pre 392 -> 373 us, entry seam 437 -> 394 us; at T = 128:
+// 56 -> 45 and 51 -> 40 us).  The one-workgroup-per-token form above stays for
+// the delayed forms' collapse workgroups and the standalone collapse, where it
+// is faster (standalone at T = 16384: 146 vs 164 us).  Same exact-order collapse
+// and folded norm; the sum of squares is taken per lane over its chunks in
+// order, then over the wave, so with the norm the two forms may differ in the
+// last bit of the norm factor.
+constexpr int kWaveCollapseMaxC = 5120;
+template <bool kBcast>
+__device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok, float p0, float p1, float p2,
+                                                    float p3) {
+  constexpr int kCh = kWaveCollapseMaxC / 8 / kWave;   // chunks per lane at most
+  constexpr int kCG = 5;                               // chunks loaded together
+  const int lane = threadIdx.x & (kWave - 1);
+  const int C8 = p.C >> 3;
+  const uint4* xs = reinterpret_cast<const uint4*>(p.x) + (size_t)tok * (kBcast ? C8 : kNS * C8);
+  uint4* lo = reinterpret_cast<uint4*>(p.li) + (size_t)tok * C8;
+  const uint4* w8 = reinterpret_cast<const uint4*>(p.nw);
+  const bool norm = p.nw != nullptr;
+  float y[kCh][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int g0 = 0; g0 < kCh; g0 += kCG) {
+    uint4 q[kCG][4];
+#pragma unroll
+    for (int u = 0; u < kCG; ++u) {
+      const int c8 = lane + (g0 + u) * kWave;
+      if (c8 < C8) {
+        q[u][0] = xs[c8];
+        q[u][1] = kBcast ? q[u][0] : xs[C8 + c8];
+        q[u][2] = kBcast ? q[u][0] : xs[2 * C8 + c8];
+        q[u][3] = kBcast ? q[u][0] : xs[3 * C8 + c8];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCG; ++u) {
+      const int ch = g0 + u;
+      const int c8 = lane + ch * kWave;
+      if (c8 < C8) {
+        collapse8(q[u][0], q[u][1], q[u][2], q[u][3], p0, p1, p2, p3, y[ch]);
+        if (norm) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(y[ch][e], y[ch][e], ss);
+        } else {
+          lo[c8] = pack8(y[ch]);
+        }
+      }
+    }
+  }
+  if (!norm) return;
+  const float tot = wave_sum(ss);
+  const float ry = 1.0f / sqrtf(tot / (float)p.C + p.eps);
+#pragma unroll
+  for (int ch = 0; ch < kCh; ++ch) {
+    const int c8 = lane + ch * kWave;
+    if (c8 < C8) {
+      float w[8], o[8];
+      unpack8(w8[c8], w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (y[ch][e] * ry) * w[e];
+      lo[c8] = pack8(o);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ pre kernel, split form
 // Workgroups [0, nproj): projection of a 16-token tile over one K-split.  With
 // nsplit > 1 the last split of a tile to arrive (counter in the workspace)
@@ -421,9 +491,15 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   __syncthreads();
   // ---- collapse with this seam's own pre-mix, token by token
   const int nt = min(kTileT, p.T - t0);
-  for (int k = 0; k < nt; ++k)
-    collapse_norm_token<MODE == kModeEntry>(p, t0 + k, s_pre[k][0], s_pre[k][1], s_pre[k][2],
-                                             s_pre[k][3], &s_tmp[0]);
+  if (p.C <= kWaveCollapseMaxC) {
+    for (int k = wave; k < nt; k += kThreads / kWave)
+      collapse_token_wave<MODE == kModeEntry>(p, t0 + k, s_pre[k][0], s_pre[k][1], s_pre[k][2],
+                                                      s_pre[k][3]);
+  } else {
+    for (int k = 0; k < nt; ++k)
+      collapse_norm_token<MODE == kModeEntry>(p, t0 + k, s_pre[k][0], s_pre[k][1], s_pre[k][2],
+                                               s_pre[k][3], &s_tmp[0]);
+  }
 }
 
 // ------------------------------------------------------------------ pre kernel, persistent delayed form
