@@ -243,6 +243,7 @@ def main():
 
     del x, x_next, li, y
     torch.cuda.empty_cache()
+    chain = None if args.no_sweep else run_chain(torch, M, mi, dev, bf, f32)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -276,6 +277,7 @@ def main():
         "two_call_seam": two_call,
         "us_per_call_sweep": sweep,
         "entry": entry,
+        "seam_chain": chain,
     }
     print(json.dumps(line), flush=True)
 
@@ -359,6 +361,69 @@ def run_entry(torch, M, mi, dev, bf, f32):
                                    for _ in range(n)], torch, reps=3, iters=20 if T > 1024 else 100)
         res[str(T)] = {"us": round(us, 2), "alg_GBps": round(entry_bytes(T) / (us * 1e-6) / 1e9, 1)}
         del o, h
+    return res
+
+
+def run_chain(torch, M, mi, dev, bf, f32, n_seams=80):
+    """Configuration 4: the model-entry seam, then 80 seams with their own weights
+    (seed 1000 + k, fused norm), the sublayer an identity stand-in (y = layer_input),
+    each seam one mhc_post_pre_delayed launch, and the last post.  The whole chain
+    is captured once in a HIP graph and replayed; reported per T: microseconds per
+    seam (chain time / 80) and the chain's time."""
+    ew = mi.entry_inputs(1, seed=999)
+    we = M.make_weights(f32(ew["fn"]), f32(ew["bias"]), f32(ew["alpha"]))
+    nw_e = bf(ew["norm_weight"])
+    seams = []
+    for k in range(n_seams):
+        sw = mi.sweep_seam_weights(k, C=C)
+        seams.append((M.make_weights(f32(sw["fn"]), f32(sw["bias"]), f32(sw["alpha"])), bf(sw["norm_weight"])))
+    res = {}
+    T = 1
+    while T <= T_SEAM:
+        h = bf(mi.entry_inputs(T, seed=999)["h"])
+        ws = M.workspace(dev, T, C)
+        sets = []
+        for _ in range(2):
+            sets.append((torch.empty((T, NS, C), dtype=torch.bfloat16, device=dev),) +
+                        tuple(M._pre_outputs(T, C, dev)))
+        x_fin = torch.empty((T, NS, C), dtype=torch.bfloat16, device=dev)
+
+        def chain():
+            a = sets[0]
+            M.mhc_broadcast_entry(h, we, nw_e, 1e-6, 20, out=a, ws=ws)
+            for k in range(n_seams):
+                b = sets[(k + 1) % 2]
+                # inputs: seam k's x, layer_input, gates and pre-mix; outputs: seam k+1's
+                M.mhc_post_pre_delayed(a[4], a[0], a[2], a[3], a[1], seams[k][0], seams[k][1], 1e-6, 20,
+                                       out=b, ws=ws)
+                a = b
+            M.mhc_post(a[4], a[0], a[2], a[3], out=x_fin)
+
+        chain()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                chain()
+        torch.cuda.current_stream().wait_stream(st)
+        g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            s0 = torch.cuda.Event(enable_timing=True)
+            e0 = torch.cuda.Event(enable_timing=True)
+            s0.record()
+            g.replay()
+            e0.record()
+            e0.synchronize()
+            times.append(s0.elapsed_time(e0))
+        ms = statistics.median(times)
+        res[str(T)] = {"us_per_seam": round(ms * 1e3 / n_seams, 2), "chain_ms": round(ms, 3)}
+        del g, sets, x_fin, h
+        torch.cuda.empty_cache()
+        T *= 2
     return res
 
 
