@@ -84,11 +84,13 @@ size_t mhc_fn_packed_bytes(int K);
  * call.  K must be a multiple of 32 and at most 4*16384. */
 mhc_status mhc_pack_fn(const float *fn, int K, void *fn_packed, void *stream);
 
-/* Workspace bytes needed by mhc_pre, mhc_pre_delayed and mhc_broadcast_entry
- * for any T <= T_max with this n and C (small token counts split the
- * projection over workgroups and combine partial sums in it).  The caller
- * zero-fills the workspace once after allocating it; every call leaves its
- * counters back at zero, so it can be reused (and captured) without clearing. */
+/* Workspace bytes needed by mhc_pre, mhc_pre_delayed, mhc_post_pre_delayed and
+ * mhc_broadcast_entry for any T <= T_max with this n and C (few tokens: the
+ * projection is split over workgroups that combine partial sums in it; with
+ * C = 5120 and T >= 256 the delayed forms' persistent kernels exchange partial
+ * sums through it).  One workspace serves all of these calls.  The caller
+ * zero-fills it once after allocating it; every call leaves its counters back
+ * at zero, so it can be reused (and captured) without clearing. */
 size_t mhc_workspace_bytes(int T_max, int n, int C);
 
 /* Pre stage, seam collapsed with its own pre-mix (p1 Purpose: the V4 form).
