@@ -126,7 +126,9 @@ mhc_status mhc_pre_delayed(const uint16_t *x, const float *pre_in, int T, int n,
 
 /* Post stage (p1 Result, the mhc_post call sites):
  *   out[t][i][c] = bf16(post[t][i] * y[t][c] + sum_j comb[t][i][j] * x[t][j][c])
- * evaluated in float, rounded once.  y [T][C] bf16 is the sublayer output,
+ * evaluated in float as fl(post_i * y) followed by one fused multiply-add per
+ * j = 0..3 in order, rounded once (the same bits as mhc_post_pre_delayed's
+ * x_out).  y [T][C] bf16 is the sublayer output,
  * x [T][n][C] bf16 the residual, post [T][n] and comb [T][n][n] float from
  * the pre stage.  out [T][n][C] bf16 may be exactly x (in place); any other
  * overlap is MHC_ERR_ALIAS.  No workspace. */
