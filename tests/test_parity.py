@@ -550,3 +550,39 @@ def test_config4_seam_chain(T):
     say("config 4 T=%d: free chain worst gate rel err over 80 seams %.2e, final residual rel L2 err %.2e"
         % (T, worst, rel))
     assert worst <= CHAIN_GATE_RTOL and rel <= CHAIN_X_RTOL
+
+
+# ----------------------------------------------------------------------------- other hidden sizes
+
+@pytest.mark.parametrize("Cx,T", [(256, 1), (256, 300), (1024, 37), (7168, 5), (7168, 300), (16384, 37)])
+def test_other_hidden_sizes(Cx, T):
+    """Hidden sizes other than 5120 (any multiple of 256 up to 16384; the split forms
+    serve them at every T): own pre-mix, delayed with norm, the fused seam, the entry
+    seam and the standalone collapse against the oracle."""
+    torch = torch_mod()
+    d = mi.pre_inputs(T, seed=1600 + Cx + T, C=Cx, delayed=True, norm=True)
+    x, nw, pin = dev_bf16(d["x"]), dev_bf16(d["norm_weight"]), dev_f32(d["pre_in"])
+    w = weights(d)
+    say("hidden %d T=%d" % (Cx, T))
+    pre, post, comb, li = M.mhc_pre(x, w, None, d["eps"], d["iters"])
+    o = oracle.mhc_pre(d["x"], d["fn"], d["bias"], d["alpha"], d["eps"], d["iters"])
+    ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"], "pre")
+    check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="pre layer_input")
+    pre_out, post, comb, li = run_delayed(d)
+    o = oracle_delayed(d)
+    check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "delayed")
+    check_bf16(li, o["li_val"], o["li_mag"], what="delayed layer_input")
+    p, post_k, comb_k = post_gates(T, seed=1700 + T)
+    y = mi.post_inputs(T, seed=1701, C=Cx)["y"]
+    check_fused(run_fused(d, y, post_k, comb_k), d, y, post_k, comb_k, what="fused")
+    e = mi.entry_inputs(T, seed=1800 + T, C=Cx)
+    x_out, pre_e, post_e, comb_e, li_e = M.mhc_broadcast_entry(dev_bf16(e["h"]), weights(e), dev_bf16(e["norm_weight"]),
+                                                              e["eps"], e["iters"])
+    oe = oracle.mhc_broadcast_entry(e["h"], e["fn"], e["bias"], e["alpha"], e["eps"], e["iters"],
+                                    norm_weight=e["norm_weight"])
+    assert np.array_equal(host_bits(x_out), oe["x_out"])
+    ge = check_gates(host_f32(pre_e), host_f32(post_e), host_f32(comb_e), oe["pre"], oe["post"], oe["comb"], "entry")
+    check_bf16(host_bits(li_e), oe["li_val"], oe["li_mag"], d=2 * ge, what="entry layer_input")
+    out = host_bits(M.mhc_collapse(x, pin))
+    torch.cuda.synchronize()
+    assert np.array_equal(out, mi.f32_to_bf16_bits(oracle.collapse32(d["x"], d["pre_in"])))
