@@ -152,6 +152,15 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
       uint4 v1 = kBcast ? v0 : xs[C8 + c8];
       uint4 v2 = kBcast ? v0 : xs[2 * C8 + c8];
       uint4 v3 = kBcast ? v0 : xs[3 * C8 + c8];
+      if (kBcast) {
+        // the entry seam's residual: h broadcast to the four streams, whole rows
+        uint4* xo = reinterpret_cast<uint4*>(p.xout) + (size_t)tok * kNS * C8 + c8;
+        xo[0] = v0;
+        xo[C8] = v0;
+        xo[2 * C8] = v0;
+        xo[3 * C8] = v0;
+        if (p.li == nullptr) continue;
+      }
       if (kPost) {
         float yv[8], a0[8], a1[8], a2[8], a3[8];
         unpack8(reinterpret_cast<const uint4*>(p.ysub)[(size_t)tok * C8 + c8], yv);
@@ -178,7 +187,7 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
       }
     }
   }
-  if (!norm) return;
+  if (!norm || (kBcast && p.li == nullptr)) return;
   const float tot = block_sum(ss, s_tmp);
   const float ry = 1.0f / sqrtf(tot / (float)p.C + p.eps);
 #pragma unroll
@@ -238,6 +247,15 @@ __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok,
       const int ch = g0 + u;
       const int c8 = lane + ch * kWave;
       if (c8 < C8) {
+        if (kBcast) {
+          // the entry seam's residual: h broadcast to the four streams, whole rows
+          uint4* xo = reinterpret_cast<uint4*>(p.xout) + (size_t)tok * kNS * C8 + c8;
+          xo[0] = q[u][0];
+          xo[C8] = q[u][0];
+          xo[2 * C8] = q[u][0];
+          xo[3 * C8] = q[u][0];
+          if (p.li == nullptr) continue;
+        }
         collapse8(q[u][0], q[u][1], q[u][2], q[u][3], p0, p1, p2, p3, y[ch]);
         if (norm) {
 #pragma unroll
@@ -248,7 +266,7 @@ __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok,
       }
     }
   }
-  if (!norm) return;
+  if (!norm || (kBcast && p.li == nullptr)) return;
   const float tot = wave_sum(ss);
   const float ry = 1.0f / sqrtf(tot / (float)p.C + p.eps);
 #pragma unroll
@@ -391,16 +409,6 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
         acc0 = mfma_bf16(xv[j], b0[j], acc0);
         acc1 = mfma_bf16(xv[j], b1[j], acc1);
         acc2 = mfma_bf16(xv[j], b2[j], acc2);
-        if (MODE == kModeEntry && valid) {
-          // broadcast h to the four streams while it is in registers
-          const size_t c = (size_t)kb * kKB + g * 8;
-          uint4* xo = reinterpret_cast<uint4*>(p.xout + (size_t)tok * kNS * p.C + c);
-          const size_t C8 = (size_t)(p.C >> 3);
-          xo[0] = xv[j];
-          xo[C8] = xv[j];
-          xo[2 * C8] = xv[j];
-          xo[3 * C8] = xv[j];
-        }
       }
     }
   }
@@ -487,7 +495,8 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
 
   if (wave == 0) tile_gates(p, s_P, t0, s_pre);
 
-  if (MODE == kModeDelayed || MODE == kModeFused || p.li == nullptr) return;
+  // the entry seam always goes on: its collapse pass also writes the broadcast residual
+  if (MODE == kModeDelayed || MODE == kModeFused || (MODE != kModeEntry && p.li == nullptr)) return;
   __syncthreads();
   // ---- collapse with this seam's own pre-mix, token by token
   const int nt = min(kTileT, p.T - t0);

@@ -581,6 +581,10 @@ def test_other_hidden_sizes(Cx, T):
     oe = oracle.mhc_broadcast_entry(e["h"], e["fn"], e["bias"], e["alpha"], e["eps"], e["iters"],
                                     norm_weight=e["norm_weight"])
     assert np.array_equal(host_bits(x_out), oe["x_out"])
+    x2, pre2, _, _, li2 = M.mhc_broadcast_entry(dev_bf16(e["h"]), weights(e), dev_bf16(e["norm_weight"]), e["eps"],
+                                                e["iters"], layer_input=False)
+    torch.cuda.synchronize()
+    assert li2 is None and np.array_equal(host_bits(x2), oe["x_out"]) and torch.equal(pre2, pre_e)
     ge = check_gates(host_f32(pre_e), host_f32(post_e), host_f32(comb_e), oe["pre"], oe["post"], oe["comb"], "entry")
     check_bf16(host_bits(li_e), oe["li_val"], oe["li_mag"], d=2 * ge, what="entry layer_input")
     out = host_bits(M.mhc_collapse(x, pin))
