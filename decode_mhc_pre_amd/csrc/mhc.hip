@@ -17,25 +17,35 @@ using namespace mhc;
 // Few tokens: the 4C row of a 16-token tile is split over workgroups, which
 // spreads the (L2/HBM-resident) projection weight over the chip; the last
 // split to arrive sums the partials.  More splits shorten the weight reads and
-// lengthen that sum.  Measured on MI355X (delayed pre, C = 5120, graph replay),
-// the best split count per tile count: 16 splits for 1-2 tiles (T <= 32),
-// 8 for 3-4, 4 for 5-16, 2 for 17-32, none beyond (e.g. T = 1: 10.9 us with 16
-// splits vs 17.5 us with 80; T = 128: 20.8 vs 25.6 us with 16).
-constexpr int kMaxSplitTiles = 32;  // tiles beyond which the row is never split
-constexpr int kMinKBPerSplit = 8;   // two 32-k steps per wave at least
-int splits_for(int ntile) {
-  return ntile <= 2 ? 16 : ntile <= 4 ? 8 : ntile <= 16 ? 4 : ntile <= kMaxSplitTiles ? 2 : 1;
+// lengthen that sum.  Split counts per tile count, measured on MI355X (C =
+// 5120, graph replay, the delayed pre): 32 splits for 1-2 tiles (T = 1:
+// 8.6 us against 9.1 us with 16), 16 for 3-4, 8 up to 64 tiles (T = 128:
+// 12.3 us against 15.7 us with 4; T = 1024: 21.0 us), 4 up to 128 and 2 up
+// to 256 tiles (T = 2048: 34.4 us, T = 4096: 63.9 us).  The forms that
+// collapse with their own pre-mix (mhc_pre, the entry seam) do the collapse in
+// each tile's last arriver and stop splitting past 128 tiles (T = 4096: 72 us
+// unsplit against 82 us with 2 splits).
+constexpr int kMaxSplitTiles = 256;     // tiles beyond which the row is never split
+constexpr int kMaxSplitTilesOwn = 128;  // the same for the forms with their own pre-mix
+int splits_for(int ntile, bool delayed) {
+  if (ntile > (delayed ? kMaxSplitTiles : kMaxSplitTilesOwn)) return 1;
+  return ntile <= 2 ? 32 : ntile <= 4 ? 16 : ntile <= 64 ? 8 : ntile <= 128 ? 4 : 2;
 }
+constexpr int kMinKBPerSplit = 8;   // two 32-k steps per wave at least
 constexpr int kMaxC = 16384;
-// The persistent delayed kernel keeps a tile's collapsed rows on chip and
-// splits each 64-token tile over a group of 16 workgroups.  Measured against
-// the split form (graph replay, C = 5120): even at T = 256 (four groups) it
-// ties for the delayed pre (25.8 vs 25.4 us) and wins for the fused seam
-// (32.7 vs 43.9 us); from T = 512 on it wins both (30 vs 35, 37 vs 69 us).
+// The persistent kernels keep a tile's collapsed rows on chip and split each
+// 64-token tile over a group of 16 workgroups; they win once the split form's
+// per-tile weight reads and duplicate residual reads (projection and collapse
+// workgroups) outweigh its parallelism.  Measured (graph replay, C = 5120):
+// delayed pre, split vs persistent, T = 1024: 21.0 vs 37.7 us, T = 4096: 63.9
+// vs 66.8 us, T = 8192: 177 vs 117 us; fused seam (post kernel + delayed split
+// kernel vs the persistent fused kernel), T = 1024: 42.2 vs 44.9 us, T = 1536:
+// 62.5 vs 54.7 us.
 constexpr int kGroupC = 5120;
-constexpr int kGroupMinT = 256;
-// Fused seam below kGroupMinT: the split kernel's fused mode is the fastest
-// form up to 8 tokens (T = 1: 12.4 us vs 13.7 us for two launches); from 16
+constexpr int kDelayedSplitMaxT = 4096;  // delayed pre: split form up to here, persistent beyond
+constexpr int kFusedGroupSplitMaxT = 1024;  // fused seam: the same threshold
+// Fused seam with few tokens: the split kernel's fused mode is the fastest
+// form up to 8 tokens (T = 1: 10.4 us vs 12.5 us for two launches); from 16
 // tokens on, the post kernel followed by the delayed split kernel is (T = 16:
 // 15.4 vs 17.7 us; T = 128: 26.9 vs 39.7 us).
 constexpr int kFusedSplitMaxT = 8;
@@ -45,11 +55,15 @@ struct Plan {
   bool persist;  // persistent delayed form (C = 5120, many tokens)
 };
 
-Plan make_plan(int T, int KB, bool persist_ok) {
+// form: kModePre / kModeEntry (own pre-mix), kModeDelayed or kModeFused;
+// persist_ok: the persistent kernels exist for this hidden size.
+Plan make_plan(int T, int KB, int form, bool persist_ok) {
   Plan pl;
   pl.ntile = (T + kTileT - 1) / kTileT;
-  pl.persist = persist_ok && T >= kGroupMinT;
-  int ns = pl.persist ? 1 : splits_for(pl.ntile);
+  const bool delayed = form == kModeDelayed || form == kModeFused;
+  pl.persist = persist_ok && ((form == kModeDelayed && T > kDelayedSplitMaxT) ||
+                              (form == kModeFused && T > kFusedGroupSplitMaxT));
+  int ns = pl.persist ? 1 : splits_for(pl.ntile, delayed);
   int maxs = KB / kMinKBPerSplit;
   if (maxs < 1) maxs = 1;
   if (ns > maxs) ns = maxs;
@@ -66,7 +80,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // read in every call) share the region from 128 KiB.
 //   [0, 256)            persistent form: word 0 finished waves, word 2 wait-budget flag
 //   [256, 82176)        persistent form: arrival counters [group][wave][5], 256 B apart
-//   [96 KiB, +128)      split form: tile counters [ntile] u32 (ntile <= 32 whenever split)
+//   [96 KiB, +1 KiB)    split form: tile counters [ntile] u32 (ntile <= 256 whenever split)
 //   [128 KiB, ...)      split form: partials [ntile][nsplit][16][25] f32, or
 //                       persistent form: records [group][wave][4] (1 KB + 32 KB each)
 constexpr size_t kSplitCntOffset = 96 * 1024;
@@ -192,7 +206,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   if (any_alias(outs, 6, ins, 9)) return MHC_ERR_ALIAS;
 
   if (T == 0) return MHC_OK;
-  Plan pl = make_plan(T, KB, delayed && C == kGroupC);
+  Plan pl = make_plan(T, KB, mode, C == kGroupC);
   const size_t need = plan_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return MHC_ERR_WORKSPACE;
 
@@ -251,7 +265,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
       return launched();
     }
     // a device too small for one group: the split form (its workspace need is covered)
-    pl = make_plan(T, KB, false);
+    pl = make_plan(T, KB, mode, false);
     p.ntile = pl.ntile;
     p.nsplit = pl.nsplit;
     p.nproj = pl.nproj;
@@ -304,13 +318,15 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
   const int ntile_max = (T_max + kTileT - 1) / kTileT;
   for (int KB : KBs) {
     for (int nt = 1; nt <= ntile_max && nt <= kMaxSplitTiles; ++nt) {
-      const Plan pl = make_plan(nt * kTileT, KB, false);
-      const size_t b = plan_ws_bytes(pl);
-      if (b > best) best = b;
+      for (int form : {kModePre, kModeDelayed}) {
+        const Plan pl = make_plan(nt * kTileT, KB, form, false);
+        const size_t b = plan_ws_bytes(pl);
+        if (b > best) best = b;
+      }
     }
   }
-  // the persistent delayed form: fixed size
-  if (C == kGroupC && T_max >= kGroupMinT && persist_ws_bytes() > best) best = persist_ws_bytes();
+  // the persistent forms: fixed size
+  if (C == kGroupC && T_max > kFusedGroupSplitMaxT && persist_ws_bytes() > best) best = persist_ws_bytes();
   return best;
 }
 

@@ -97,6 +97,22 @@ __device__ __forceinline__ void buf_store16(uint4 v, rsrc_t r, int voff, int sof
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
 }
 
+// ---------------------------------------------------------------- device-coherent access
+// Values passed between workgroups (which may sit on different XCDs, each with
+// its own L2) use agent-scope atomic loads and stores: each is coherent on its
+// own, so no fence has to write back or invalidate an L2.
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory access of the wave has completed (stores
+// included); also a compiler barrier for memory.
+__device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------- quad shuffles (DPP)
 // Lane l reads lane l^1 / l^2 of its quad; all 64 lanes must be active.
 __device__ __forceinline__ float dpp_quad_xor1(float v) {

@@ -79,7 +79,8 @@ __global__ __launch_bounds__(256) void mhc_pack_fn_kernel(const float* __restric
 // over the four lanes of a quad (DPP), so every lane of a column divides by the
 // same bits.  The row maximum is subtracted before exp (removed exactly by the
 // first row step); reciprocals are the hardware's (error <= 1 ulp).
-__device__ __forceinline__ void tile_gates(const PreParams& p, const float (*s_P)[kPS], int t0,
+// `ba` holds bias[24] then alpha[3] (LDS).
+__device__ __forceinline__ void tile_gates(const PreParams& p, const float* ba, const float (*s_P)[kPS], int t0,
                                            float (*s_pre)[kNS], bool write = true) {
   const int lane = threadIdx.x & (kWave - 1);
   const int tt = lane >> 2;
@@ -87,10 +88,10 @@ __device__ __forceinline__ void tile_gates(const PreParams& p, const float (*s_P
   const int tk = t0 + tt;
   const bool ok = tk < p.T;
   const float r = 1.0f / sqrtf(s_P[tt][24] / (float)p.K + p.eps);
-  const float ac = p.alpha[2];
+  const float ac = ba[kNL + 2];
   float m[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) m[j] = ac * (r * s_P[tt][8 + 4 * row + j]) + p.bias[8 + 4 * row + j];
+  for (int j = 0; j < 4; ++j) m[j] = ac * (r * s_P[tt][8 + 4 * row + j]) + ba[8 + 4 * row + j];
   const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
 #pragma unroll
   for (int j = 0; j < 4; ++j) m[j] = expf(m[j] - mx);
@@ -105,8 +106,8 @@ __device__ __forceinline__ void tile_gates(const PreParams& p, const float (*s_P
       m[j] *= __builtin_amdgcn_rcpf(c);
     }
   }
-  const float lp = p.alpha[0] * (r * s_P[tt][row]) + p.bias[row];
-  const float lq = p.alpha[1] * (r * s_P[tt][4 + row]) + p.bias[4 + row];
+  const float lp = ba[kNL] * (r * s_P[tt][row]) + ba[row];
+  const float lq = ba[kNL + 1] * (r * s_P[tt][4 + row]) + ba[4 + row];
   const float pr = 1.0f / (1.0f + expf(-lp));
   const float po = 2.0f / (1.0f + expf(-lq));
   s_pre[tt][row] = pr;
@@ -301,6 +302,7 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   __shared__ float s_P[kTileT][kPS];
   __shared__ float s_pre[kTileT][kNS];
   __shared__ float s_tmp[4];
+  __shared__ float s_ba[32];   // bias[24], alpha[3]
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
@@ -322,6 +324,9 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   const int t0 = tile * kTileT;
   const int tok = t0 + li_;
   const bool valid = tok < p.T;
+  // bias and alpha, loaded now and staged in LDS with the first barrier, so
+  // that the gates after the reduction wait on no global load
+  const float bav = tid < kNL ? p.bias[tid] : (tid >= 32 && tid < 35) ? p.alpha[tid - 32] : 0.f;
   const int kb0 = (int)(((long long)sp * p.KB) / p.nsplit);
   const int kb1 = (int)(((long long)(sp + 1) * p.KB) / p.nsplit);
 
@@ -423,6 +428,8 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
     s_red[wave][4 * g + r][32 + li_] = acc2[r];
   }
   if (g == 0) s_red[wave][li_][48] = ssq;
+  if (tid < kNL) s_ba[tid] = bav;
+  if (tid >= 32 && tid < 35) s_ba[kNL + tid - 32] = bav;
   __syncthreads();
 
   // thread (tt, q): token row tt = tid >> 4, logit q (and q + 16 when q < 8)
@@ -447,19 +454,24 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   }
 
   if (p.nsplit > 1) {
+    // The partials cross workgroups (and XCDs) through device-coherent stores
+    // and loads, each coherent on its own: no fence, so no write-back or
+    // invalidation of the L2 (which would also drop the cached weight).  A
+    // wave's stores are complete once its store counter drains, before the
+    // workgroup's arrival is counted; the last arriver's loads are ordered
+    // after its counter update by the barrier and its control dependence.
     float* dst = p.part + ((size_t)(tile * p.nsplit + sp) * kTileT + tt) * kPartStride;
-    dst[q] = v0;
-    if (q < 8) dst[16 + q] = v1;
-    if (q == 15) dst[24] = vs;
-    __threadfence();
+    st_agent(dst + q, v0);
+    if (q < 8) st_agent(dst + 16 + q, v1);
+    if (q == 15) st_agent(dst + 24, vs);
+    wait_vmem();
     __syncthreads();
     if (tid == 0) {
-      const unsigned old = atomicAdd(&p.cnt[tile], 1u);
+      const unsigned old = __hip_atomic_fetch_add(&p.cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = (old == (unsigned)(p.nsplit - 1));
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     // sum the partials of every split in split order; each (token, value) pair
     // is one thread, and its loads are issued kRedChunk at a time
     const float* src = p.part + (size_t)tile * p.nsplit * kTileT * kPartStride;
@@ -476,7 +488,7 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
             float v[kRedChunk];
 #pragma unroll
             for (int u = 0; u < kRedChunk; ++u)
-              v[u] = (s0 + u < p.nsplit) ? __builtin_nontemporal_load(src + (s0 + u) * sstride + pair) : 0.f;
+              v[u] = (s0 + u < p.nsplit) ? ld_agent(src + (s0 + u) * sstride + pair) : 0.f;
 #pragma unroll
             for (int u = 0; u < kRedChunk; ++u)
               if (s0 + u < p.nsplit) acc += v[u];
@@ -485,7 +497,7 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
         s_P[pt][pv] = acc;
       }
     }
-    if (tid == 0) atomicExch(&p.cnt[tile], 0u);  // leave the workspace as found
+    if (tid == 0) st_agent(&p.cnt[tile], 0u);  // leave the workspace as found
   } else {
     s_P[tt][q] = v0;
     if (q < 8) s_P[tt][16 + q] = v1;
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   }
   __syncthreads();
 
-  if (wave == 0) tile_gates(p, s_P, t0, s_pre);
+  if (wave == 0) tile_gates(p, s_ba, s_P, t0, s_pre);
 
   // the entry seam always goes on: its collapse pass also writes the broadcast residual
   if (MODE == kModeDelayed || MODE == kModeFused || (MODE != kModeEntry && p.li == nullptr)) return;
@@ -626,10 +638,6 @@ inline size_t persist_ws_bytes() {
 __device__ __forceinline__ void buf_store16_agent(uint4 v, rsrc_t r, int voff, int soff) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 16);
 }
-__device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 constexpr int kWaitVmem0 = 0x0f70;   // s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained (gfx9 encoding)
 constexpr int kAuxAgent = 16;    // buffer cache policy: coherent at device scope (sc1)
 __device__ __forceinline__ uint4 buf_load16_agent(rsrc_t r, int voff, int soff) {

@@ -38,10 +38,12 @@ def test_sizes():
     assert m.mhc_fn_packed_bytes(4 * C) == 4 * C * 24 * 4
     assert m.mhc_fn_packed_bytes(0) == 0
     assert m.mhc_workspace_bytes(1, 4, C) > 0
-    # few tokens: split partials, bounded; many tokens (persistent delayed
-    # form): a fixed set of exchange records, whatever the token count
+    # up to 1024 tokens only split partials, bounded; beyond (the persistent
+    # fused form, then the persistent delayed form): a fixed set of exchange
+    # records, whatever the token count
     assert m.mhc_workspace_bytes(128, 4, C) < 2 * MiB
-    assert m.mhc_workspace_bytes(256, 4, C) == m.mhc_workspace_bytes(16384, 4, C)
+    assert m.mhc_workspace_bytes(1024, 4, C) < 2 * MiB
+    assert m.mhc_workspace_bytes(1025, 4, C) == m.mhc_workspace_bytes(16384, 4, C)
     assert m.mhc_workspace_bytes(16384, 4, C) < 16 * MiB
     assert m.mhc_workspace_bytes(1 << 20, 4, C) == m.mhc_workspace_bytes(16384, 4, C)
     assert m.mhc_workspace_bytes(1 << 20, 4, 4096) < 2 * MiB   # no grouped form for C != 5120
@@ -169,11 +171,17 @@ def test_entry_specific():
 
 
 def test_workspace_needs_by_form():
-    # T >= 2048, delayed, C = 5120: grouped form, partial sums go through the workspace
+    # delayed, C = 5120, T > 4096: persistent form, partial sums go through the workspace
+    assert call_delayed(T=6001, ws=None) == WS
+    assert call_delayed(T=6001, ws_bytes=m.mhc_workspace_bytes(6001, 4, C) - 16) == WS
+    assert call_delayed(T=6001, ws_bytes=m.mhc_workspace_bytes(6001, 4, C)) == HIP
+    # delayed at 4096 tokens: split form (2 splits per tile), partials in the workspace
     assert call_delayed(T=4096, ws=None) == WS
-    assert call_delayed(T=4096, ws_bytes=m.mhc_workspace_bytes(4096, 4, C) - 16) == WS
     assert call_delayed(T=4096, ws_bytes=m.mhc_workspace_bytes(4096, 4, C)) == HIP
-    # own pre-mix at T >= 2048: one workgroup per 16-token tile, nothing to combine
+    # own pre-mix: split up to 128 tiles (T = 2048), beyond that one workgroup
+    # per 16-token tile, nothing to combine
+    assert call_pre(T=2048, ws=None) == WS
+    assert call_pre(T=2049, ws=None) == HIP
     assert call_pre(T=4096, ws=None) == HIP
 
 

@@ -262,14 +262,15 @@ def test_config2_prefill_delayed_norm_sampled():
     assert np.array_equal(li_nn, mi.f32_to_bf16_bits(y32))
 
 
-@pytest.mark.parametrize("T", [2048, 2113, 3999])
-def test_persistent_delayed_every_token(T):
-    """Token counts served by the persistent delayed kernel (64-token tiles
-    over groups of 16 workgroups; several tiles per group, ragged last tile,
-    groups with unequal tile counts), checked on every token; without the
-    norm the layer input is the exact-order collapse, bit for bit."""
+@pytest.mark.parametrize("T", [2113, 4096, 4097, 6001])
+def test_delayed_many_tokens_every_token(T):
+    """Many tokens, checked on every token: the split form with 2-4 splits per
+    tile (2113, 4096 tokens) and the persistent delayed kernel from 4097 tokens
+    (64-token tiles over groups of 16 workgroups; several tiles per group,
+    ragged last tile, groups with unequal tile counts).  Without the norm the
+    layer input is the exact-order collapse, bit for bit."""
     d = mi.pre_inputs(T, seed=40 + T, delayed=True, norm=True, outlier_frac=0.01)
-    say("persistent delayed T=%d" % T)
+    say("delayed many tokens T=%d" % T)
     pre_out, post, comb, li = run_delayed(d)
     o = oracle_delayed(d)
     check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "persist T=%d" % T)
@@ -284,13 +285,13 @@ def test_persistent_repeat_and_workspace_reset():
     """The persistent kernel's arrival counters are back at zero after every
     call: calls of different sizes on one workspace repeat bit for bit."""
     torch = torch_mod()
-    ds = {T: mi.pre_inputs(T, seed=800 + T, delayed=True, norm=True) for T in (4096, 2048)}
-    first = {T: run_delayed(ds[T]) for T in (4096, 2048)}
-    for T in (2048, 4096, 2048):
+    ds = {T: mi.pre_inputs(T, seed=800 + T, delayed=True, norm=True) for T in (6001, 4160)}
+    first = {T: run_delayed(ds[T]) for T in (6001, 4160)}
+    for T in (4160, 6001, 4160):
         again = run_delayed(ds[T])
         for u, v in zip(first[T], again):
             assert np.array_equal(u, v)
-    ws = M.workspace(torch.device("cuda"), 4096, C)
+    ws = M.workspace(torch.device("cuda"), 6001, C)
     assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
 
 
@@ -309,7 +310,7 @@ def test_standalone_collapse(T):
     check_bf16(outn, o["li_val"], o["li_mag"], what="collapse T=%d" % T)
 
 
-@pytest.mark.parametrize("T", [100, 2113])
+@pytest.mark.parametrize("T", [100, 4160])
 def test_standalone_collapse_equals_delayed_layer_input(T):
     """Without the norm, mhc_collapse(x, p) is bit-identical to the layer_input of
     mhc_pre_delayed(x, pre_in = p), on both pre-kernel forms (split and persistent)."""
@@ -339,7 +340,7 @@ def test_repeatable_and_workspace_reset():
     """Split-K runs leave the workspace counters at zero: back-to-back calls on
     one workspace, with different token counts, give identical bits."""
     torch = torch_mod()
-    for T in (1, 64, 1):
+    for T in (1, 64, 2113, 1):
         d = mi.pre_inputs(T, seed=700, delayed=True, norm=True)
         a = run_delayed(d)
         b = run_delayed(d)
@@ -393,7 +394,7 @@ def test_post_pre_delayed(T, norm):
     check_fused(run_fused(d, y, post, comb), d, y, post, comb, what="fused T=%d" % T)
 
 
-@pytest.mark.parametrize("T", [5, 300, 4100])
+@pytest.mark.parametrize("T", [5, 300, 1100, 4100])
 def test_post_pre_delayed_equals_two_calls(T):
     """The fused form against mhc_post followed by mhc_pre_delayed: the residual bit
     for bit, layer_input without the norm bit for bit; the gates, and layer_input
@@ -417,14 +418,15 @@ def test_post_pre_delayed_equals_two_calls(T):
             assert np.array_equal(a[4], lb)
 
 
-@pytest.mark.parametrize("T", [2048, 2113, 3999])
-def test_persistent_fused_every_token(T):
-    """Token counts served by the persistent fused kernel (the persistent delayed
-    kernel with the post stage in front), every token against the oracle
-    composition, with the norm and without it."""
+@pytest.mark.parametrize("T", [1024, 1025, 2113, 3999])
+def test_fused_many_tokens_every_token(T):
+    """Many tokens of the fused seam, every token against the oracle
+    composition, with the norm and without it: the post kernel followed by the
+    delayed split kernel (1024 tokens) and the persistent fused kernel (the
+    persistent delayed kernel with the post stage in front) from 1025."""
     for norm in (True, False):
         d, y, post, comb = fused_case(T, 1300 + T, norm, outlier_frac=0.01)
-        say("persistent fused T=%d norm=%s" % (T, norm))
+        say("fused many tokens T=%d norm=%s" % (T, norm))
         check_fused(run_fused(d, y, post, comb), d, y, post, comb, what="persist fused T=%d" % T)
 
 
