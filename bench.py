@@ -103,6 +103,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the T=1..128 sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU oracle sample time")
+    ap.add_argument("--sweep-only", default=None, metavar="T,...",
+                    help="only the per-call latency sweep (eager and graph replay) at these token counts")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -130,6 +132,16 @@ def main():
 
     def f32(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    if args.sweep_only:
+        # decode-size latency only (e.g. for a kernel trace of the small-T kernels)
+        d = mi.pre_inputs(8, seed=2, delayed=True, norm=True)
+        w = M.make_weights(f32(d["fn"]), f32(d["bias"]), f32(d["alpha"]))
+        Ts = tuple(int(t) for t in args.sweep_only.split(","))
+        print(json.dumps({"us_per_call_sweep": run_sweep(torch, M, mi, dev, bf, f32, w, bf(d["norm_weight"]), Ts),
+                          "config": {"workload": "mhc seam ops at decode sizes, n=4, C=5120, fused RMSNorm, "
+                                                 "20 Sinkhorn iters", "T": list(Ts)}}), flush=True)
+        return
 
     # ---------------------------------------------------------------- seam inputs (HBM-resident)
     t0 = time.time()
@@ -296,9 +308,9 @@ def _median_us(fn, torch, reps=5, iters=200):
     return statistics.median(out)
 
 
-def run_sweep(torch, M, mi, dev, bf, f32, w, nw):
+def run_sweep(torch, M, mi, dev, bf, f32, w, nw, Ts=SWEEP_T):
     res = {}
-    for T in SWEEP_T:
+    for T in Ts:
         d = mi.pre_inputs(T, seed=50 + T, delayed=True)
         x = bf(d["x"])
         pin = f32(d["pre_in"])
