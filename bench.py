@@ -321,6 +321,12 @@ def run_sweep(torch, M, mi, dev, bf, f32, w, nw, Ts=SWEEP_T):
         def pre_call():
             M.mhc_pre_delayed(x, pin, w, nw, 1e-6, 20, out=outs, ws=ws)
 
+        outs_own = M._pre_outputs(T, C, dev)
+
+        def own_call():
+            # the non-delayed form (own pre-mix, no norm: configuration 0's op)
+            M.mhc_pre(x, w, None, 1e-6, 20, out=outs_own, ws=ws)
+
         def post_call():
             M.mhc_post(outs[3], x, outs[1], outs[2], out=xo)
 
@@ -335,8 +341,8 @@ def run_sweep(torch, M, mi, dev, bf, f32, w, nw, Ts=SWEEP_T):
             M.mhc_post_pre_delayed(outs[3], x, outs[1], outs[2], pin, w, nw, 1e-6, 20, out=fo, ws=ws)
 
         row = {}
-        for name, fn in (("pre_delayed", pre_call), ("post", post_call), ("seam", seam_call),
-                         ("seam_fused", fused_call)):
+        for name, fn in (("pre_delayed", pre_call), ("pre_own", own_call), ("post", post_call),
+                         ("seam", seam_call), ("seam_fused", fused_call)):
             fn()
             torch.cuda.synchronize()
             # eager: host launch path included

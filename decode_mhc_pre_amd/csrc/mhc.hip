@@ -80,11 +80,14 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // read in every call) share the region from 128 KiB.
 //   [0, 256)            persistent form: word 0 finished waves, word 2 wait-budget flag
 //   [256, 82176)        persistent form: arrival counters [group][wave][5], 256 B apart
-//   [96 KiB, +1 KiB)    split form: tile counters [ntile] u32 (ntile <= 256 whenever split)
+//   [96 KiB, +4 KiB)    split form: tile counters [ntile] u32 (ntile <= 256 whenever split),
+//                       then (256 words apart) own-pre-mix ready flags [ntile], their done
+//                       counts [ntile] and the wait-ran-out word
 //   [128 KiB, ...)      split form: partials [ntile][nsplit][16][25] f32, or
 //                       persistent form: records [group][wave][4] (1 KB + 32 KB each)
 constexpr size_t kSplitCntOffset = 96 * 1024;
-static_assert(kSplitCntOffset + kMaxSplitTiles * sizeof(unsigned) <= kPPartOffset,
+static_assert(kMaxSplitTiles <= kSplitFlagStride, "split tile counters overlap the ready flags");
+static_assert(kSplitCntOffset + kSplitWords * sizeof(unsigned) <= kPPartOffset,
               "split counters overlap the data region");
 static_assert(kPCntBase * 4 + (size_t)kPMaxGroups * 4 * kPSlots * kPCntStride * 4 <= kSplitCntOffset,
               "persistent counters overlap the split counters");
@@ -210,7 +213,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   const size_t need = plan_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return MHC_ERR_WORKSPACE;
 
-  PreParams p;
+  PreParams p{};
   p.x = x;
   p.pre_in = pre_in;
   p.fnp = static_cast<const uint4*>(w.fn_packed);
@@ -242,6 +245,10 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   p.ntile = pl.ntile;
   p.nsplit = pl.nsplit;
   p.nproj = pl.nproj;
+  // own pre-mix, split projection: one collapse workgroup per token, waiting
+  // for its tile's pre-mix (instead of the tile's last arriver collapsing all
+  // of its tokens after the gates)
+  p.own_wgs = (!delayed && pl.nsplit > 1 && C <= kWaveCollapseMaxC) ? 1 : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 block(kThreads);
@@ -273,7 +280,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   }
   switch (mode) {
     case kModePre:
-      hipLaunchKernelGGL(mhc_pre_split_kernel<kModePre>, dim3(pl.nproj), block, 0, s, p);
+      hipLaunchKernelGGL(mhc_pre_split_kernel<kModePre>, dim3(pl.nproj + (p.own_wgs ? T : 0)), block, 0, s, p);
       break;
     case kModeDelayed:
       hipLaunchKernelGGL(mhc_pre_split_kernel<kModeDelayed>, dim3(pl.nproj + T), block, 0, s, p);
@@ -282,7 +289,8 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
       hipLaunchKernelGGL(mhc_pre_split_kernel<kModeFused>, dim3(pl.nproj + T), block, 0, s, p);
       break;
     default:
-      hipLaunchKernelGGL(mhc_pre_split_kernel<kModeEntry>, dim3(pl.nproj), block, 0, s, p);
+      hipLaunchKernelGGL(mhc_pre_split_kernel<kModeEntry>, dim3(pl.nproj + (p.own_wgs ? T : 0)), block, 0, s,
+                         p);
       break;
   }
   return launched();

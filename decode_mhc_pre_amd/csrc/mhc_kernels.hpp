@@ -41,9 +41,19 @@ struct PreParams {
   int iters;
   int T, C, K, KB;        // K = row length, KB = K / 32
   int ntile, nsplit, nproj;
+  int own_wgs;            // own pre-mix: workgroups [nproj, nproj + T) collapse one token each
 };
 
 constexpr int kPS = 28;      // LDS row per token: P[0..23], sum x^2 [24], sum y^2 [25]
+// Split-form words after the tile arrival counters (p.cnt[tile]), in 32-bit
+// words from p.cnt: per-tile "pre-mix ready" flags, per-tile counts of
+// collapse workgroups done with the flag, and a word set when a wait ran out.
+constexpr int kSplitFlagStride = 256;          // at least the most tiles a split call has
+constexpr int kSplitReady = kSplitFlagStride;
+constexpr int kSplitDone = 2 * kSplitFlagStride;
+constexpr int kSplitWaitErr = 3 * kSplitFlagStride;
+constexpr int kSplitWords = 3 * kSplitFlagStride + 1;
+constexpr int kOwnWaitBudget = 1 << 20;        // sleeps per collapse workgroup (about a second)
 constexpr int kJMax = 8;     // k-steps a wave issues together in the split kernel
 constexpr int kRedChunk = 16;  // partials loaded together by the last arriver
 
@@ -113,7 +123,7 @@ __device__ __forceinline__ void tile_gates(const PreParams& p, const float* ba, 
   s_pre[tt][row] = pr;
   if (ok && write) {
     reinterpret_cast<float4*>(p.comb)[(size_t)tk * 4 + row] = make_float4(m[0], m[1], m[2], m[3]);
-    p.pre[(size_t)tk * kNS + row] = pr;
+    st_agent(&p.pre[(size_t)tk * kNS + row], pr);   // read by other workgroups (own-pre-mix collapse)
     p.post[(size_t)tk * kNS + row] = po;
   }
 }
@@ -283,6 +293,111 @@ __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok,
   }
 }
 
+// ------------------------------------------------------------------ own pre-mix collapse, waiting workgroup
+// One workgroup per token, for the forms that collapse with the seam's own
+// pre-mix (mhc_pre, the entry seam) when the projection is split: the token's
+// residual row is loaded first, then the workgroup waits until its tile's last
+// arriving projection workgroup has published the pre-mix (flag kSplitReady),
+// so the collapse overlaps the projection instead of following it in one
+// workgroup per tile.  The entry seam writes its broadcast residual before
+// waiting, and does not wait at all when no layer_input is requested.
+// Forward progress: projection workgroups have the lower indices and are
+// dispatched first; none of them waits for anything.  The wait is bounded
+// nevertheless (kOwnWaitBudget sleeps): if it runs out the workgroup records
+// it in p.cnt[kSplitWaitErr] and goes on, so the kernel always ends.
+// Hidden sizes up to kWaveCollapseMaxC (3 chunks of 8 per thread).
+template <bool kBcast>
+__device__ __forceinline__ void collapse_own_token(const PreParams& p, int tok, float* s_tmp, float* s_pm) {
+  constexpr int kCh = 3;
+  const int tid = threadIdx.x;
+  const int C8 = p.C >> 3;
+  const uint4* xs = reinterpret_cast<const uint4*>(p.x) + (size_t)tok * (kBcast ? C8 : kNS * C8);
+  uint4 q[kCh][4];
+#pragma unroll
+  for (int s = 0; s < kCh; ++s) {
+    const int c8 = tid + s * kThreads;
+    if (c8 < C8) {
+      q[s][0] = xs[c8];
+      q[s][1] = kBcast ? q[s][0] : xs[C8 + c8];
+      q[s][2] = kBcast ? q[s][0] : xs[2 * C8 + c8];
+      q[s][3] = kBcast ? q[s][0] : xs[3 * C8 + c8];
+    }
+  }
+  if (kBcast) {
+#pragma unroll
+    for (int s = 0; s < kCh; ++s) {
+      const int c8 = tid + s * kThreads;
+      if (c8 < C8) {
+        uint4* xo = reinterpret_cast<uint4*>(p.xout) + (size_t)tok * kNS * C8 + c8;
+        xo[0] = q[s][0];
+        xo[C8] = q[s][0];
+        xo[2 * C8] = q[s][0];
+        xo[3 * C8] = q[s][0];
+      }
+    }
+    if (p.li == nullptr) return;
+  }
+  const int tile = tok / kTileT;
+  if (tid == 0) {
+    unsigned* ready = p.cnt + kSplitReady + tile;
+    int budget = kOwnWaitBudget;
+    unsigned v = ld_agent(ready);
+    while (v == 0u && budget > 0) {
+      --budget;
+      __builtin_amdgcn_s_sleep(2);
+      v = ld_agent(ready);
+    }
+    if (v == 0u) st_agent(p.cnt + kSplitWaitErr, 1u);
+    __asm__ volatile("" ::: "memory");   // the pre-mix loads follow the flag
+#pragma unroll
+    for (int i = 0; i < kNS; ++i) s_pm[i] = ld_agent(&p.pre[(size_t)tok * kNS + i]);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // the last of the tile's collapse workgroups to get past the flag clears it
+    const int ntok = min(kTileT, p.T - tile * kTileT);
+    const unsigned old = __hip_atomic_fetch_add(p.cnt + kSplitDone + tile, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (unsigned)(ntok - 1)) {
+      st_agent(p.cnt + kSplitReady + tile, 0u);
+      st_agent(p.cnt + kSplitDone + tile, 0u);
+    }
+  }
+  const float p0 = s_pm[0], p1 = s_pm[1], p2 = s_pm[2], p3 = s_pm[3];
+  uint4* lo = reinterpret_cast<uint4*>(p.li) + (size_t)tok * C8;
+  const bool norm = p.nw != nullptr;
+  float y[kCh][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int s = 0; s < kCh; ++s) {
+    const int c8 = tid + s * kThreads;
+    if (c8 < C8) {
+      collapse8(q[s][0], q[s][1], q[s][2], q[s][3], p0, p1, p2, p3, y[s]);
+      if (norm) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(y[s][e], y[s][e], ss);
+      } else {
+        lo[c8] = pack8(y[s]);
+      }
+    }
+  }
+  if (!norm) return;
+  const float tot = block_sum(ss, s_tmp);
+  const float ry = 1.0f / sqrtf(tot / (float)p.C + p.eps);
+  const uint4* w8 = reinterpret_cast<const uint4*>(p.nw);
+#pragma unroll
+  for (int s = 0; s < kCh; ++s) {
+    const int c8 = tid + s * kThreads;
+    if (c8 < C8) {
+      float w[8], o[8];
+      unpack8(w8[c8], w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (y[s][e] * ry) * w[e];
+      lo[c8] = pack8(o);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ pre kernel, split form
 // Workgroups [0, nproj): projection of a 16-token tile over one K-split.  With
 // nsplit > 1 the last split of a tile to arrive (counter in the workspace)
@@ -302,6 +417,7 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   __shared__ float s_P[kTileT][kPS];
   __shared__ float s_pre[kTileT][kNS];
   __shared__ float s_tmp[4];
+  __shared__ float s_pm[4];    // own-pre-mix collapse workgroups: the token's pre-mix
   __shared__ float s_ba[32];   // bias[24], alpha[3]
   __shared__ int s_last;
 
@@ -312,6 +428,10 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
     const int tok = b - p.nproj;
     const float4 pin = reinterpret_cast<const float4*>(p.pre_in)[tok];
     collapse_norm_token<false, MODE == kModeFused>(p, tok, pin.x, pin.y, pin.z, pin.w, &s_tmp[0]);
+    return;
+  }
+  if ((MODE == kModePre || MODE == kModeEntry) && p.own_wgs && b >= p.nproj) {
+    collapse_own_token<MODE == kModeEntry>(p, b - p.nproj, &s_tmp[0], &s_pm[0]);
     return;
   }
 
@@ -506,6 +626,16 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   __syncthreads();
 
   if (wave == 0) tile_gates(p, s_ba, s_P, t0, s_pre);
+
+  if ((MODE == kModePre || MODE == kModeEntry) && p.own_wgs) {
+    // the collapse workgroups of this tile take it from here: publish the
+    // pre-mix (wave 0's device-coherent stores, drained) and flag it
+    if (wave == 0 && p.li != nullptr) {
+      wait_vmem();
+      if (lane == 0) st_agent(p.cnt + kSplitReady + tile, 1u);
+    }
+    return;
+  }
 
   // the entry seam always goes on: its collapse pass also writes the broadcast residual
   if (MODE == kModeDelayed || MODE == kModeFused || (MODE != kModeEntry && p.li == nullptr)) return;

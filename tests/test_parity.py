@@ -66,9 +66,11 @@ def test_pack_fn_split_and_layout():
 
 # ----------------------------------------------------------------------------- pre, delayed, entry
 
-@pytest.mark.parametrize("T", [1, 2, 7, 8, 17, 128, 1000])
+@pytest.mark.parametrize("T", [1, 2, 7, 8, 17, 128, 1000, 2048, 2049])
 def test_pre_no_norm(T):
-    """Configuration 0 (T = 8, no norm) and neighbours: own pre-mix."""
+    """Configuration 0 (T = 8, no norm) and neighbours: own pre-mix.  Up to 2048
+    tokens the projection is split and one workgroup per token collapses once
+    its tile's pre-mix is published; from 2049 each tile's workgroup does it."""
     d = mi.pre_inputs(T, seed=100 + T)
     x = dev_bf16(d["x"])
     pre, post, comb, li = M.mhc_pre(x, weights(d), None, d["eps"], d["iters"])
@@ -88,6 +90,37 @@ def test_pre_with_norm(T):
     say("mhc_pre T=%d norm" % T)
     ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"])
     check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="layer_input")
+
+
+def test_own_premix_repeat_and_workspace_reset():
+    """The own-pre-mix forms' collapse workgroups wait on per-tile flags in the
+    workspace: back-to-back mhc_pre and entry calls of different sizes on one
+    workspace repeat bit for bit, and every flag, count and the wait-ran-out
+    word are back at zero afterwards."""
+    torch = torch_mod()
+    ds = {T: mi.pre_inputs(T, seed=1600 + T, norm=True) for T in (1, 17, 300)}
+    es = {T: mi.entry_inputs(T, seed=1700 + T) for T in (1, 17, 300)}
+
+    def pre(T):
+        d = ds[T]
+        return [host_bits(t) if t.dtype == torch.bfloat16 else host_f32(t)
+                for t in M.mhc_pre(dev_bf16(d["x"]), weights(d), dev_bf16(d["norm_weight"]), d["eps"], d["iters"])]
+
+    def entry(T, li):
+        d = es[T]
+        out = M.mhc_broadcast_entry(dev_bf16(d["h"]), weights(d), dev_bf16(d["norm_weight"]), d["eps"], d["iters"],
+                                    layer_input=li)
+        return [None if t is None else host_bits(t) if t.dtype == torch.bfloat16 else host_f32(t) for t in out]
+
+    first = {T: (pre(T), entry(T, True), entry(T, False)) for T in (1, 17, 300)}
+    for T in (17, 300, 1, 17):
+        say("own pre-mix repeat T=%d" % T)
+        again = (pre(T), entry(T, True), entry(T, False))
+        for a, b in zip(first[T], again):
+            for u, v in zip(a, b):
+                assert (u is None and v is None) or np.array_equal(u, v)
+    ws = M.workspace(torch.device("cuda"), 300, C)
+    assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
 
 
 @pytest.mark.parametrize("T", [1, 2, 7, 16, 128, 1024])
