@@ -451,17 +451,21 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   const int kb1 = (int)(((long long)(sp + 1) * p.KB) / p.nsplit);
 
   // ---- projection over this split's k-blocks: wave w takes kb0 + w, +4, ...,
-  // issuing up to kJMax steps' loads before the first MFMA.
-  const uint16_t* xrow = p.x + (size_t)(valid ? tok : 0) * p.K + g * 8;
+  // issuing up to kJMax steps' loads before the first MFMA.  Residual rows
+  // through a descriptor covering the tile's tokens: rows past the last token
+  // read as zero without a memory access.
+  const int ntok = min(kTileT, p.T - t0);
+  const rsrc_t xr = make_rsrc(p.x + (size_t)t0 * p.K, ntok * p.K * 2);
+  const int xoff = li_ * p.K * 2 + g * 16;   // bytes: the lane's row and 8-column group
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
   float ssq = 0.f;
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
   if constexpr (MODE == kModeFused) {
     // column blocks [cbA, cbB) of all four streams; wave w takes cbA + w, +4, ...
     const int CB = p.C / kKB;
     const int cbA = (int)(((long long)sp * CB) / p.nsplit);
     const int cbB = (int)(((long long)(sp + 1) * CB) / p.nsplit);
-    const uint16_t* yrow = p.ysub + (size_t)(valid ? tok : 0) * p.C + g * 8;
+    const rsrc_t yr = make_rsrc(p.ysub + (size_t)t0 * p.C, ntok * p.C * 2);
+    const int yoff = li_ * p.C * 2 + g * 16;
     float pw[4] = {0.f, 0.f, 0.f, 0.f};
     float4 cr[4];
 #pragma unroll
@@ -481,10 +485,10 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
       for (int j = 0; j < kJFused; ++j) {
         const int cb = base + 4 * j;
         if (cb < cbB) {
-          yv[j] = valid ? *reinterpret_cast<const uint4*>(yrow + (size_t)cb * kKB) : zero;
+          yv[j] = buf_load16(yr, yoff + cb * kKB * 2, 0);
 #pragma unroll
           for (int s = 0; s < kNS; ++s) {
-            xv[j][s] = valid ? *reinterpret_cast<const uint4*>(xrow + (size_t)s * p.C + (size_t)cb * kKB) : zero;
+            xv[j][s] = buf_load16(xr, xoff + (s * p.C + cb * kKB) * 2, 0);
             const uint4* bp = p.fnp + (size_t)(s * CB + cb) * (kFragPerKB * kWave) + lane;
 #pragma unroll
             for (int f = 0; f < kFragPerKB; ++f) bw[j][s][f] = bp[f * kWave];
@@ -519,7 +523,7 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
     for (int j = 0; j < kJMax; ++j) {
       const int kb = base + 4 * j;
       if (kb < kb1) {
-        xv[j] = valid ? *reinterpret_cast<const uint4*>(xrow + (size_t)kb * kKB) : zero;
+        xv[j] = buf_load16(xr, xoff + kb * kKB * 2, 0);
         const uint4* bp = p.fnp + (size_t)kb * (kFragPerKB * kWave) + lane;
         b0[j] = bp[0];
         b1[j] = bp[kWave];
