@@ -55,7 +55,7 @@ constexpr int kSplitWaitErr = 3 * kSplitFlagStride;
 constexpr int kSplitWords = 3 * kSplitFlagStride + 1;
 constexpr int kOwnWaitBudget = 1 << 20;        // sleeps per collapse workgroup (about a second)
 constexpr int kJMax = 8;     // k-steps a wave issues together in the split kernel
-constexpr int kRedChunk = 16;  // partials loaded together by the last arriver
+constexpr int kRedChunk = 32;  // partials loaded together by the last arriver
 
 // ------------------------------------------------------------------ packing
 // Packed layout: for 32-row block kb and column tile q (0..2, columns 16q..16q+15
