@@ -252,6 +252,7 @@ def main():
     if not args.no_sweep:
         sweep = run_sweep(torch, M, mi, dev, bf, f32, w, nw)
     entry = None if args.no_sweep else run_entry(torch, M, mi, dev, bf, f32)
+    collapse = None if args.no_sweep else run_collapse(torch, M, x, pre_in, nw)
 
     del x, x_next, li, y
     torch.cuda.empty_cache()
@@ -289,6 +290,7 @@ def main():
         "two_call_seam": two_call,
         "us_per_call_sweep": sweep,
         "entry": entry,
+        "collapse": collapse,
         "seam_chain": chain,
     }
     print(json.dumps(line), flush=True)
@@ -380,6 +382,19 @@ def run_entry(torch, M, mi, dev, bf, f32):
         res[str(T)] = {"us": round(us, 2), "alg_GBps": round(entry_bytes(T) / (us * 1e-6) / 1e9, 1)}
         del o, h
     return res
+
+
+def run_collapse(torch, M, x, pin, nw):
+    """The standalone collapse (exact-order collapse + folded norm) on the seam's
+    residual: one kernel, T x (40,960 + 16) bytes read, T x 10,240 written."""
+    T = x.shape[0]
+    out = M.mhc_collapse(x, pin, nw, 1e-6)
+    torch.cuda.synchronize()
+    us = _median_us(lambda n: [M.mhc_collapse(x, pin, nw, 1e-6, out=out) for _ in range(n)], torch,
+                    reps=3, iters=20)
+    nbytes = T * (NS * C * 2 + 16 + C * 2) + C * 2
+    return {"T": T, "us": round(us, 2), "alg_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def run_chain(torch, M, mi, dev, bf, f32, n_seams=80):
