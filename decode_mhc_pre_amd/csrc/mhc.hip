@@ -39,11 +39,13 @@ constexpr int kMaxC = 16384;
 // workgroups) outweigh its parallelism.  Measured (graph replay, C = 5120):
 // delayed pre, split vs persistent, T = 1024: 21.0 vs 37.7 us, T = 4096: 63.9
 // vs 66.8 us, T = 8192: 177 vs 117 us; fused seam (post kernel + delayed split
-// kernel vs the persistent fused kernel), T = 1024: 42.2 vs 44.9 us, T = 1536:
-// 62.5 vs 54.7 us.
+// kernel vs the persistent fused kernel), T = 1100: 50.0 vs 56.9 us, T = 1280:
+// 55.1 vs 55.7 us, T = 1536: 62.4 vs 54.7 us (at 1025-1280 tokens some groups
+// of the persistent grid take two tiles and others one); delayed pre at T =
+// 4160: 83.1 vs 73.8 us.
 constexpr int kGroupC = 5120;
 constexpr int kDelayedSplitMaxT = 4096;  // delayed pre: split form up to here, persistent beyond
-constexpr int kFusedGroupSplitMaxT = 1024;  // fused seam: the same threshold
+constexpr int kFusedGroupSplitMaxT = 1280;  // fused seam: the same threshold
 // Fused seam with few tokens: the split kernel's fused mode is the fastest
 // form up to 8 tokens (T = 1: 10.4 us vs 12.5 us for two launches); from 16
 // tokens on, the post kernel followed by the delayed split kernel is (T = 16:
