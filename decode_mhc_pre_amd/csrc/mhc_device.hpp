@@ -124,6 +124,17 @@ __device__ __forceinline__ float dpp_quad_xor2(float v) {
                                                                0xF, 0xF, false));
 }
 
+// Rotations within a 16-lane DPP row: lane l reads lane (l - 8) mod 16 (the
+// same as lane l ^ 8) / (l - 4) mod 16 of its row.
+__device__ __forceinline__ float dpp_row_ror8(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128,
+                                                               0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_ror4(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124,
+                                                               0xF, 0xF, false));
+}
+
 // ---------------------------------------------------------------- collapse
 // y_c = fl(fl(fl(fl(p0 x0) + fl(p1 x1)) + fl(p2 x2)) + fl(p3 x3)): each product
 // rounded to float, summed left to right over the streams, never fused --

@@ -84,48 +84,49 @@ __global__ __launch_bounds__(256) void mhc_pack_fn_kernel(const float* __restric
 }
 
 // ------------------------------------------------------------------ gates + Sinkhorn
-// One full wave handles a 16-token tile: lane L owns token L >> 2 and comb row
-// L & 3 (four entries).  Row sums stay in the lane; column sums are a butterfly
-// over the four lanes of a quad (DPP), so every lane of a column divides by the
-// same bits.  The row maximum is subtracted before exp (removed exactly by the
-// first row step); reciprocals are the hardware's (error <= 1 ulp).
-// `ba` holds bias[24] then alpha[3] (LDS).
+// The four waves of the workgroup take a 16-token tile, four tokens each: a
+// token's 16 lanes (one DPP row) hold its 4x4 comb matrix, lane 4i + j entry
+// (i, j), so an iteration is two butterflies, two reciprocals and two
+// multiplies per lane.  Row sums: quad butterflies; column sums: rotations of
+// the 16-lane row by 8 (the same as exchanging with lane ^ 8) and then by 4,
+// which pairs (0,2) and (1,3) in every lane.  Either way every lane of a row
+// or column divides by the same bits.  The row maximum is subtracted before
+// exp (removed exactly by the first row step); reciprocals are the hardware's
+// (error <= 1 ulp).  The lanes of row 0 also make the token's pre and post
+// gates (gate index j).  `ba` holds bias[24] then alpha[3] (LDS).
 __device__ __forceinline__ void tile_gates(const PreParams& p, const float* ba, const float (*s_P)[kPS], int t0,
-                                           float (*s_pre)[kNS], bool write = true) {
+                                           float (*s_pre)[kNS]) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int tt = lane >> 2;
-  const int row = lane & 3;
+  const int tt = (threadIdx.x / kWave) * 4 + (lane >> 4);
+  const int i = (lane >> 2) & 3;
+  const int j = lane & 3;
   const int tk = t0 + tt;
   const bool ok = tk < p.T;
   const float r = 1.0f / sqrtf(s_P[tt][24] / (float)p.K + p.eps);
-  const float ac = ba[kNL + 2];
-  float m[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) m[j] = ac * (r * s_P[tt][8 + 4 * row + j]) + ba[8 + 4 * row + j];
-  const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) m[j] = expf(m[j] - mx);
+  float m = ba[kNL + 2] * (r * s_P[tt][8 + 4 * i + j]) + ba[8 + 4 * i + j];
+  float mx = fmaxf(m, dpp_quad_xor1(m));
+  mx = fmaxf(mx, dpp_quad_xor2(mx));
+  m = expf(m - mx);
   for (int it = 0; it < p.iters; ++it) {
-    const float inv = __builtin_amdgcn_rcpf((m[0] + m[1]) + (m[2] + m[3]));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] *= inv;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float c = m[j] + dpp_quad_xor1(m[j]);
-      c = c + dpp_quad_xor2(c);
-      m[j] *= __builtin_amdgcn_rcpf(c);
+    float rs = m + dpp_quad_xor1(m);
+    rs = rs + dpp_quad_xor2(rs);
+    m *= __builtin_amdgcn_rcpf(rs);
+    float cs = m + dpp_row_ror8(m);
+    cs = cs + dpp_row_ror4(cs);
+    m *= __builtin_amdgcn_rcpf(cs);
+  }
+  if (i == 0) {
+    const float lp = ba[kNL] * (r * s_P[tt][j]) + ba[j];
+    const float lq = ba[kNL + 1] * (r * s_P[tt][4 + j]) + ba[4 + j];
+    const float pr = 1.0f / (1.0f + expf(-lp));
+    const float po = 2.0f / (1.0f + expf(-lq));
+    s_pre[tt][j] = pr;
+    if (ok) {
+      st_agent(&p.pre[(size_t)tk * kNS + j], pr);   // read by other workgroups (own-pre-mix collapse)
+      p.post[(size_t)tk * kNS + j] = po;
     }
   }
-  const float lp = ba[kNL] * (r * s_P[tt][row]) + ba[row];
-  const float lq = ba[kNL + 1] * (r * s_P[tt][4 + row]) + ba[4 + row];
-  const float pr = 1.0f / (1.0f + expf(-lp));
-  const float po = 2.0f / (1.0f + expf(-lq));
-  s_pre[tt][row] = pr;
-  if (ok && write) {
-    reinterpret_cast<float4*>(p.comb)[(size_t)tk * 4 + row] = make_float4(m[0], m[1], m[2], m[3]);
-    st_agent(&p.pre[(size_t)tk * kNS + row], pr);   // read by other workgroups (own-pre-mix collapse)
-    p.post[(size_t)tk * kNS + row] = po;
-  }
+  if (ok) p.comb[(size_t)tk * 16 + 4 * i + j] = m;
 }
 
 // ------------------------------------------------------------------ collapse + norm, one token
@@ -629,14 +630,15 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   }
   __syncthreads();
 
-  if (wave == 0) tile_gates(p, s_ba, s_P, t0, s_pre);
+  tile_gates(p, s_ba, s_P, t0, s_pre);
 
   if ((MODE == kModePre || MODE == kModeEntry) && p.own_wgs) {
     // the collapse workgroups of this tile take it from here: publish the
-    // pre-mix (wave 0's device-coherent stores, drained) and flag it
-    if (wave == 0 && p.li != nullptr) {
+    // pre-mix (every wave's device-coherent stores, drained) and flag it
+    if (p.li != nullptr) {
       wait_vmem();
-      if (lane == 0) st_agent(p.cnt + kSplitReady + tile, 1u);
+      __syncthreads();
+      if (tid == 0) st_agent(p.cnt + kSplitReady + tile, 1u);
     }
     return;
   }
@@ -807,7 +809,8 @@ __device__ __forceinline__ unsigned zero_after(unsigned v) {
 // (P[24], sum x^2) sit in `v`; `ba` holds bias[24] then alpha[3] (both LDS:
 // no global load here, whose wait would also wait for every x load in
 // flight).  Every quad of the wave computes the same token (lane & 3 = comb
-// row); quad 0 writes.  Same arithmetic as tile_gates.
+// row); quad 0 writes.  The same gates and Sinkhorn as tile_gates, one comb
+// row per lane.
 struct TokenGates {
   float m[4];
   float pr, po;
