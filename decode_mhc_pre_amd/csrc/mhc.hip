@@ -39,18 +39,18 @@ constexpr int kMaxC = 16384;
 // workgroups) outweigh its parallelism.  Measured (graph replay, C = 5120):
 // delayed pre, split vs persistent, T = 1024: 21.0 vs 37.7 us, T = 4096: 63.9
 // vs 66.8 us, T = 8192: 177 vs 117 us; fused seam (post kernel + delayed split
-// kernel vs the persistent fused kernel), T = 1100: 50.0 vs 56.9 us, T = 1280:
-// 55.1 vs 55.7 us, T = 1536: 62.4 vs 54.7 us (at 1025-1280 tokens some groups
-// of the persistent grid take two tiles and others one); delayed pre at T =
-// 4160: 83.1 vs 73.8 us.
+// kernel's fused mode vs the persistent fused kernel), T = 1281: 36.2 vs 54.9
+// us, T = 2048: 55.0 vs 59.7 us, T = 3072: 79.6 vs 94.2 us, T = 4096: 135.7 vs
+// 118.3 us; delayed pre at T = 4160: 83.1 vs 73.8 us.
 constexpr int kGroupC = 5120;
 constexpr int kDelayedSplitMaxT = 4096;  // delayed pre: split form up to here, persistent beyond
-constexpr int kFusedGroupSplitMaxT = 1280;  // fused seam: the same threshold
-// Fused seam with few tokens: the split kernel's fused mode is the fastest
-// form up to 8 tokens (T = 1: 10.4 us vs 12.5 us for two launches); from 16
-// tokens on, the post kernel followed by the delayed split kernel is (T = 16:
-// 15.4 vs 17.7 us; T = 128: 26.9 vs 39.7 us).
-constexpr int kFusedSplitMaxT = 8;
+constexpr int kFusedGroupSplitMaxT = 3072;  // fused seam: the same threshold
+// Fused seam below the persistent form: the split kernel's fused mode (one
+// launch) against the post kernel followed by the delayed split kernel, T =
+// 16: 10.8 vs 11.9 us, T = 128: 14.5 vs 18.0 us, T = 1024: 32.1 vs 41.7 us.
+// At other hidden sizes the fused mode runs up to the same token count and
+// the two launches beyond it.
+constexpr int kFusedSplitMaxT = 3072;
 
 struct Plan {
   int ntile, nsplit, nproj;
@@ -336,7 +336,8 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
     }
   }
   // the persistent forms: fixed size
-  if (C == kGroupC && T_max > kFusedGroupSplitMaxT && persist_ws_bytes() > best) best = persist_ws_bytes();
+  const int persist_min_t = (kFusedGroupSplitMaxT < kDelayedSplitMaxT ? kFusedGroupSplitMaxT : kDelayedSplitMaxT) + 1;
+  if (C == kGroupC && T_max >= persist_min_t && persist_ws_bytes() > best) best = persist_ws_bytes();
   return best;
 }
 

@@ -87,7 +87,7 @@ mhc_status mhc_pack_fn(const float *fn, int K, void *fn_packed, void *stream);
 /* Workspace bytes needed by mhc_pre, mhc_pre_delayed, mhc_post_pre_delayed and
  * mhc_broadcast_entry for any T <= T_max with this n and C (few tokens: the
  * projection is split over workgroups that combine partial sums in it; with
- * C = 5120 the persistent kernels of mhc_post_pre_delayed (T > 1280) and
+ * C = 5120 the persistent kernels of mhc_post_pre_delayed (T > 3072) and
  * mhc_pre_delayed (T > 4096) exchange partial sums through it).  One
  * workspace serves all of these calls.  The caller zero-fills it once after
  * allocating it; every call leaves its counters back
@@ -156,9 +156,8 @@ mhc_status mhc_post(const uint16_t *y, const uint16_t *x, const float *post,
  *            rounded once (the same bits as mhc_post).
  *   pre_out, post, comb, layer_input: seam k+1's outputs, from x_out, as in
  *            mhc_pre_delayed.
- * Launches: one for T <= 8 and, with C = 5120, for T > 1280; in between (and
- * for every T > 8 at other hidden sizes) the post kernel and then the delayed
- * pre kernel (measured faster there).  The
+ * Launches: one; at hidden sizes other than 5120 and T > 3072, the post kernel
+ * and then the delayed pre kernel.  The
  * workspace is that of mhc_pre_delayed (mhc_workspace_bytes).  x_out must not
  * overlap x or any other argument: this form is not in place (MHC_ERR_ALIAS). */
 mhc_status mhc_post_pre_delayed(const uint16_t *y, const uint16_t *x,

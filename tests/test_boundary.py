@@ -38,12 +38,12 @@ def test_sizes():
     assert m.mhc_fn_packed_bytes(4 * C) == 4 * C * 24 * 4
     assert m.mhc_fn_packed_bytes(0) == 0
     assert m.mhc_workspace_bytes(1, 4, C) > 0
-    # up to 1280 tokens only split partials, bounded; beyond (the persistent
+    # up to 3072 tokens only split partials, bounded; beyond (the persistent
     # fused form, then the persistent delayed form): a fixed set of exchange
     # records, whatever the token count
     assert m.mhc_workspace_bytes(128, 4, C) < 2 * MiB
-    assert m.mhc_workspace_bytes(1280, 4, C) < 2 * MiB
-    assert m.mhc_workspace_bytes(1281, 4, C) == m.mhc_workspace_bytes(16384, 4, C)
+    assert m.mhc_workspace_bytes(3072, 4, C) < 2 * MiB
+    assert m.mhc_workspace_bytes(3073, 4, C) == m.mhc_workspace_bytes(16384, 4, C)
     assert m.mhc_workspace_bytes(16384, 4, C) < 16 * MiB
     assert m.mhc_workspace_bytes(1 << 20, 4, C) == m.mhc_workspace_bytes(16384, 4, C)
     assert m.mhc_workspace_bytes(1 << 20, 4, 4096) < 2 * MiB   # no grouped form for C != 5120

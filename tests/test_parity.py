@@ -451,12 +451,12 @@ def test_post_pre_delayed_equals_two_calls(T):
             assert np.array_equal(a[4], lb)
 
 
-@pytest.mark.parametrize("T", [1280, 1281, 2113, 3999])
+@pytest.mark.parametrize("T", [1281, 3072, 3073, 3999])
 def test_fused_many_tokens_every_token(T):
     """Many tokens of the fused seam, every token against the oracle
-    composition, with the norm and without it: the post kernel followed by the
-    delayed split kernel (1280 tokens) and the persistent fused kernel (the
-    persistent delayed kernel with the post stage in front) from 1281."""
+    composition, with the norm and without it: the split kernel's fused mode
+    (up to 3072 tokens) and the persistent fused kernel (the persistent delayed
+    kernel with the post stage in front) from 3073."""
     for norm in (True, False):
         d, y, post, comb = fused_case(T, 1300 + T, norm, outlier_frac=0.01)
         say("fused many tokens T=%d norm=%s" % (T, norm))
