@@ -19,9 +19,10 @@ using namespace mhc;
 // split to arrive sums the partials.  More splits shorten the weight reads and
 // lengthen that sum.  Split counts per tile count, measured on MI355X (C =
 // 5120, graph replay, the delayed pre): 32 splits for 1-2 tiles (T = 1:
-// 8.6 us against 9.1 us with 16), 16 for 3-4, 8 up to 64 tiles (T = 128:
-// 12.3 us against 15.7 us with 4; T = 1024: 21.0 us), 4 up to 128 and 2 up
-// to 256 tiles (T = 2048: 34.4 us, T = 4096: 63.9 us).  The forms that
+// 8.6 us against 9.1 us with 16), 16 up to 16 tiles (T = 64: 9.9 us against
+// 10.2 with 32; T = 128: 10.7 us against 12.1 with 8), 8 up to 64 tiles (T =
+// 1024: 20.7 us), 4 up to 128 (T = 2048: 34.5 us against 36.1 with 8) and 2 up
+// to 256 tiles (T = 4096: 63.9 us).  The forms that
 // collapse with their own pre-mix (mhc_pre, the entry seam) do the collapse in
 // each tile's last arriver and stop splitting past 128 tiles (T = 4096: 72 us
 // unsplit against 82 us with 2 splits).
@@ -29,7 +30,7 @@ constexpr int kMaxSplitTiles = 256;     // tiles beyond which the row is never s
 constexpr int kMaxSplitTilesOwn = 128;  // the same for the forms with their own pre-mix
 int splits_for(int ntile, bool delayed) {
   if (ntile > (delayed ? kMaxSplitTiles : kMaxSplitTilesOwn)) return 1;
-  return ntile <= 2 ? 32 : ntile <= 4 ? 16 : ntile <= 64 ? 8 : ntile <= 128 ? 4 : 2;
+  return ntile <= 2 ? 32 : ntile <= 16 ? 16 : ntile <= 64 ? 8 : ntile <= 128 ? 4 : 2;
 }
 constexpr int kMinKBPerSplit = 8;   // two 32-k steps per wave at least
 constexpr int kMaxC = 16384;
