@@ -80,18 +80,21 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout.  Counters must read zero when a call starts, and one
 // workspace serves calls of both forms, so the two forms' counters live in
 // disjoint places that nothing else writes; their data (rewritten before it is
-// read in every call) share the region from 128 KiB.
+// read in every call) share the region from 192 KiB.
 //   [0, 256)            persistent form: word 0 finished waves, word 2 wait-budget flag
 //   [256, 82176)        persistent form: arrival counters [group][wave][5], 256 B apart
-//   [96 KiB, +4 KiB)    split form: tile counters [ntile] u32 (ntile <= 256 whenever split),
-//                       then (256 words apart) own-pre-mix ready flags [ntile], their done
-//                       counts [ntile] and the wait-ran-out word
-//   [128 KiB, ...)      split form: partials [ntile][nsplit][16][25] f32, or
+//   [96 KiB, +1028)     split form: tile counters [ntile] u32 (ntile <= 256 whenever split),
+//                       then the wait-ran-out word
+//   [100 KiB, +32 KiB)  split form: own-pre-mix records [T <= 2048][4] u32 (pre-mix bits
+//                       with the sign bit set; zero when empty)
+//   [192 KiB, ...)      split form: partials [ntile][nsplit][16][25] f32, or
 //                       persistent form: records [group][wave][4] (1 KB + 32 KB each)
 constexpr size_t kSplitCntOffset = 96 * 1024;
-static_assert(kMaxSplitTiles <= kSplitFlagStride, "split tile counters overlap the ready flags");
-static_assert(kSplitCntOffset + kSplitWords * sizeof(unsigned) <= kPPartOffset,
-              "split counters overlap the data region");
+static_assert(kMaxSplitTiles <= kSplitFlagStride, "split tile counters overlap the wait word");
+static_assert((kSplitFlagStride + 1) * sizeof(unsigned) <= (size_t)kSplitRecBytes,
+              "split counters overlap the own-pre-mix records");
+static_assert(kMaxSplitTilesOwn * kTileT <= kOwnMaxTokens, "own-pre-mix records too few for a split call");
+static_assert(kSplitCntOffset + kSplitBytes <= kPPartOffset, "split counters and records overlap the data region");
 static_assert(kPCntBase * 4 + (size_t)kPMaxGroups * 4 * kPSlots * kPCntStride * 4 <= kSplitCntOffset,
               "persistent counters overlap the split counters");
 size_t plan_ws_bytes(const Plan& pl) {
@@ -251,7 +254,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   // own pre-mix, split projection: one collapse workgroup per token, waiting
   // for its tile's pre-mix (instead of the tile's last arriver collapsing all
   // of its tokens after the gates)
-  p.own_wgs = (!delayed && pl.nsplit > 1 && C <= kWaveCollapseMaxC) ? 1 : 0;
+  p.own_wgs = (!delayed && pl.nsplit > 1 && C <= kWaveCollapseMaxC && T <= kOwnMaxTokens) ? 1 : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 block(kThreads);

@@ -109,6 +109,14 @@ template <typename T>
 __device__ __forceinline__ void st_agent(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The same for 16-byte buffer accesses: cache policy coherent at device scope (sc1).
+constexpr int kAuxAgent = 16;
+__device__ __forceinline__ uint4 buf_load16_agent(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAuxAgent));
+}
+__device__ __forceinline__ void buf_store16_agent(uint4 v, rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, kAuxAgent);
+}
 // Wait until every vector memory access of the wave has completed (stores
 // included); also a compiler barrier for memory.
 __device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

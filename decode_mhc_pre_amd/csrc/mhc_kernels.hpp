@@ -45,15 +45,19 @@ struct PreParams {
 };
 
 constexpr int kPS = 28;      // LDS row per token: P[0..23], sum x^2 [24], sum y^2 [25]
-// Split-form words after the tile arrival counters (p.cnt[tile]), in 32-bit
-// words from p.cnt: per-tile "pre-mix ready" flags, per-tile counts of
-// collapse workgroups done with the flag, and a word set when a wait ran out.
+// Split-form workspace from p.cnt: the tile arrival counters (32-bit words
+// [0, kSplitFlagStride)), a word set when a wait ran out (kSplitWaitErr), and
+// from byte kSplitRecBytes the own-pre-mix records, 16 bytes per token: the
+// four pre-mix values with the sign bit set.  A pre-mix value is >= 0, so a set
+// sign bit marks a written word and zero an empty one; the consumer clears its
+// record, so the region is back at zero after every call.
 constexpr int kSplitFlagStride = 256;          // at least the most tiles a split call has
-constexpr int kSplitReady = kSplitFlagStride;
-constexpr int kSplitDone = 2 * kSplitFlagStride;
-constexpr int kSplitWaitErr = 3 * kSplitFlagStride;
-constexpr int kSplitWords = 3 * kSplitFlagStride + 1;
+constexpr int kSplitWaitErr = kSplitFlagStride;
+constexpr int kSplitRecBytes = 4096;
+constexpr int kOwnMaxTokens = 2048;            // tokens an own-pre-mix call with collapse workgroups may have
+constexpr int kSplitBytes = kSplitRecBytes + kOwnMaxTokens * 16;
 constexpr int kOwnWaitBudget = 1 << 20;        // sleeps per collapse workgroup (about a second)
+constexpr unsigned kRecSet = 0x80000000u;
 constexpr int kJMax = 8;     // k-steps a wave issues together in the split kernel
 constexpr int kRedChunk = 32;  // partials loaded together by the last arriver
 
@@ -94,8 +98,9 @@ __global__ __launch_bounds__(256) void mhc_pack_fn_kernel(const float* __restric
 // exp (removed exactly by the first row step); reciprocals are the hardware's
 // (error <= 1 ulp).  The lanes of row 0 also make the token's pre and post
 // gates (gate index j).  `ba` holds bias[24] then alpha[3] (LDS).
+// `rec` (or nullptr): the own-pre-mix records the tile's collapse workgroups wait on.
 __device__ __forceinline__ void tile_gates(const PreParams& p, const float* ba, const float (*s_P)[kPS], int t0,
-                                           float (*s_pre)[kNS]) {
+                                           float (*s_pre)[kNS], unsigned* rec) {
   const int lane = threadIdx.x & (kWave - 1);
   const int tt = (threadIdx.x / kWave) * 4 + (lane >> 4);
   const int i = (lane >> 2) & 3;
@@ -122,8 +127,9 @@ __device__ __forceinline__ void tile_gates(const PreParams& p, const float* ba, 
     const float po = 2.0f / (1.0f + expf(-lq));
     s_pre[tt][j] = pr;
     if (ok) {
-      st_agent(&p.pre[(size_t)tk * kNS + j], pr);   // read by other workgroups (own-pre-mix collapse)
+      p.pre[(size_t)tk * kNS + j] = pr;
       p.post[(size_t)tk * kNS + j] = po;
+      if (rec != nullptr) st_agent(rec + (size_t)tk * kNS + j, __float_as_uint(pr) | kRecSet);
     }
   }
   if (ok) p.comb[(size_t)tk * 16 + 4 * i + j] = m;
@@ -298,9 +304,10 @@ __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok,
 // One workgroup per token, for the forms that collapse with the seam's own
 // pre-mix (mhc_pre, the entry seam) when the projection is split: the token's
 // residual row is loaded first, then the workgroup waits until its tile's last
-// arriving projection workgroup has published the pre-mix (flag kSplitReady),
-// so the collapse overlaps the projection instead of following it in one
-// workgroup per tile.  The entry seam writes its broadcast residual before
+// arriving projection workgroup has published the token's pre-mix record (the
+// four values with their sign bits set, polled with device-coherent loads and
+// cleared once read), so the collapse overlaps the projection instead of
+// following it in one workgroup per tile.  The entry seam writes its broadcast residual before
 // waiting, and does not wait at all when no layer_input is requested.
 // Forward progress: projection workgroups have the lower indices and are
 // dispatched first; none of them waits for anything.  The wait is bounded
@@ -338,32 +345,24 @@ __device__ __forceinline__ void collapse_own_token(const PreParams& p, int tok, 
     }
     if (p.li == nullptr) return;
   }
-  const int tile = tok / kTileT;
   if (tid == 0) {
-    unsigned* ready = p.cnt + kSplitReady + tile;
+    // the token's record: four words, each written with its sign bit set
+    const rsrc_t rr = make_rsrc(reinterpret_cast<char*>(p.cnt) + kSplitRecBytes, p.T * 16);
     int budget = kOwnWaitBudget;
-    unsigned v = ld_agent(ready);
-    while (v == 0u && budget > 0) {
+    uint4 v = buf_load16_agent(rr, tok * 16, 0);
+    while (((v.x & v.y & v.z & v.w) & kRecSet) == 0u && budget > 0) {
       --budget;
       __builtin_amdgcn_s_sleep(2);
-      v = ld_agent(ready);
+      v = buf_load16_agent(rr, tok * 16, 0);
     }
-    if (v == 0u) st_agent(p.cnt + kSplitWaitErr, 1u);
-    __asm__ volatile("" ::: "memory");   // the pre-mix loads follow the flag
-#pragma unroll
-    for (int i = 0; i < kNS; ++i) s_pm[i] = ld_agent(&p.pre[(size_t)tok * kNS + i]);
+    if (((v.x & v.y & v.z & v.w) & kRecSet) == 0u) st_agent(p.cnt + kSplitWaitErr, 1u);
+    buf_store16_agent(make_uint4(0u, 0u, 0u, 0u), rr, tok * 16, 0);   // consumed: back to empty
+    s_pm[0] = __uint_as_float(v.x & ~kRecSet);
+    s_pm[1] = __uint_as_float(v.y & ~kRecSet);
+    s_pm[2] = __uint_as_float(v.z & ~kRecSet);
+    s_pm[3] = __uint_as_float(v.w & ~kRecSet);
   }
   __syncthreads();
-  if (tid == 0) {
-    // the last of the tile's collapse workgroups to get past the flag clears it
-    const int ntok = min(kTileT, p.T - tile * kTileT);
-    const unsigned old = __hip_atomic_fetch_add(p.cnt + kSplitDone + tile, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (unsigned)(ntok - 1)) {
-      st_agent(p.cnt + kSplitReady + tile, 0u);
-      st_agent(p.cnt + kSplitDone + tile, 0u);
-    }
-  }
   const float p0 = s_pm[0], p1 = s_pm[1], p2 = s_pm[2], p3 = s_pm[3];
   uint4* lo = reinterpret_cast<uint4*>(p.li) + (size_t)tok * C8;
   const bool norm = p.nw != nullptr;
@@ -630,18 +629,12 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   }
   __syncthreads();
 
-  tile_gates(p, s_ba, s_P, t0, s_pre);
-
-  if ((MODE == kModePre || MODE == kModeEntry) && p.own_wgs) {
-    // the collapse workgroups of this tile take it from here: publish the
-    // pre-mix (every wave's device-coherent stores, drained) and flag it
-    if (p.li != nullptr) {
-      wait_vmem();
-      __syncthreads();
-      if (tid == 0) st_agent(p.cnt + kSplitReady + tile, 1u);
-    }
-    return;
-  }
+  const bool own = (MODE == kModePre || MODE == kModeEntry) && p.own_wgs;
+  tile_gates(p, s_ba, s_P, t0, s_pre,
+             own && p.li != nullptr ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(p.cnt) + kSplitRecBytes)
+                                    : nullptr);
+  // own pre-mix: the tile's collapse workgroups take it from here (records)
+  if (own) return;
 
   // the entry seam always goes on: its collapse pass also writes the broadcast residual
   if (MODE == kModeDelayed || MODE == kModeFused || (MODE != kModeEntry && p.li == nullptr)) return;
@@ -747,7 +740,7 @@ constexpr int kPRing = 4;        // record slots per (group, wave)
 constexpr int kPCntBase = 64;
 constexpr int kPCntStride = 64;  // words
 constexpr int kPSlots = kPRing + 1;
-constexpr size_t kPPartOffset = 128 * 1024;
+constexpr size_t kPPartOffset = 192 * 1024;
 static_assert(kPCntBase * 4 + (size_t)kPMaxGroups * (kThreads / kWave) * kPSlots * kPCntStride * 4 <= kPPartOffset,
               "arrival counters overlap the records");
 constexpr int kSpinBudget = 1 << 20;  // sleeps per wave over the whole call (about a second)
@@ -771,14 +764,7 @@ inline size_t persist_ws_bytes() {
 // Partial sums cross workgroups (and XCDs) through device-coherent accesses:
 // agent-scope atomic stores and loads, each coherent on its own, so no release
 // fence has to write back the L2.
-__device__ __forceinline__ void buf_store16_agent(uint4 v, rsrc_t r, int voff, int soff) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 16);
-}
 constexpr int kWaitVmem0 = 0x0f70;   // s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained (gfx9 encoding)
-constexpr int kAuxAgent = 16;    // buffer cache policy: coherent at device scope (sc1)
-__device__ __forceinline__ uint4 buf_load16_agent(rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAuxAgent));
-}
 // The accumulation registers (AGPRs) as parking space for values that wait a
 // tile or two: keeps the architectural registers free for the load queue.
 __device__ __forceinline__ float agpr_park(float v) {

@@ -366,7 +366,7 @@ def test_config3_post_sampled():
 
 
 # every counter of both kernel forms lies in the workspace's first 128 KiB
-COUNTER_BYTES = 128 * 1024
+COUNTER_BYTES = 192 * 1024
 
 
 def test_repeatable_and_workspace_reset():
