@@ -332,7 +332,7 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
   const int ntile_max = (T_max + kTileT - 1) / kTileT;
   for (int KB : KBs) {
     for (int nt = 1; nt <= ntile_max && nt <= kMaxSplitTiles; ++nt) {
-      for (int form : {kModePre, kModeDelayed}) {
+      for (int form : {kModePre, kModeDelayed, kModeFused}) {
         const Plan pl = make_plan(nt * kTileT, KB, form, false);
         const size_t b = plan_ws_bytes(pl);
         if (b > best) best = b;
