@@ -141,7 +141,11 @@ __device__ __forceinline__ void tile_gates(const PreParams& p, const float* ba, 
 // kPost: the streams collapsed are the post stage's output, computed here from
 // the previous residual, the sublayer output and the previous seam's gates,
 // and written out as the next residual on the way.
-template <bool kBcast, bool kPost = false>
+// kStream: the residual rows are read and layer_input written with streaming
+// (non-temporal) accesses, for a call that streams more than the memory-side
+// cache holds; the split kernel's collapse workgroups read rows its projection
+// workgroups have just read, so they keep them cached.
+template <bool kBcast, bool kPost = false, bool kStream = false>
 __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok, float p0, float p1,
                                                     float p2, float p3, float* s_tmp) {
   const int C8 = p.C >> 3;
@@ -166,10 +170,10 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
   for (int s = 0; s < 8; ++s) {
     const int c8 = threadIdx.x + s * kThreads;
     if (c8 < C8) {
-      uint4 v0 = xs[c8];
-      uint4 v1 = kBcast ? v0 : xs[C8 + c8];
-      uint4 v2 = kBcast ? v0 : xs[2 * C8 + c8];
-      uint4 v3 = kBcast ? v0 : xs[3 * C8 + c8];
+      uint4 v0 = kStream ? nt_load16(xs + c8) : xs[c8];
+      uint4 v1 = kBcast ? v0 : kStream ? nt_load16(xs + C8 + c8) : xs[C8 + c8];
+      uint4 v2 = kBcast ? v0 : kStream ? nt_load16(xs + 2 * C8 + c8) : xs[2 * C8 + c8];
+      uint4 v3 = kBcast ? v0 : kStream ? nt_load16(xs + 3 * C8 + c8) : xs[3 * C8 + c8];
       if (kBcast) {
         // the entry seam's residual: h broadcast to the four streams, whole rows
         uint4* xo = reinterpret_cast<uint4*>(p.xout) + (size_t)tok * kNS * C8 + c8;
@@ -201,7 +205,10 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(y[s][e], y[s][e], ss);
       } else {
-        lo[c8] = pack8(y[s]);
+        if (kStream)
+          nt_store16(pack8(y[s]), lo + c8);
+        else
+          lo[c8] = pack8(y[s]);
       }
     }
   }
@@ -216,7 +223,10 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
       unpack8(w8[c8], w);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (y[s][e] * ry) * w[e];
-      lo[c8] = pack8(o);
+      if (kStream)
+        nt_store16(pack8(o), lo + c8);
+      else
+        lo[c8] = pack8(o);
     }
   }
 }
@@ -1347,12 +1357,14 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
 
 // ------------------------------------------------------------------ standalone collapse
 // One workgroup per token: the exact-order collapse with p[token] and the
-// optional folded norm (collapse_norm_token), nothing else.
+// optional folded norm (collapse_norm_token), nothing else.  kStream: streaming
+// accesses (a call larger than the memory-side cache).
+template <bool kStream>
 __global__ __launch_bounds__(kThreads) void mhc_collapse_kernel(PreParams p) {
   __shared__ float s_tmp[4];
   const int tok = blockIdx.x;
   const float4 pv = reinterpret_cast<const float4*>(p.pre_in)[tok];
-  collapse_norm_token<false>(p, tok, pv.x, pv.y, pv.z, pv.w, s_tmp);
+  collapse_norm_token<false, false, kStream>(p, tok, pv.x, pv.y, pv.z, pv.w, s_tmp);
 }
 
 // ------------------------------------------------------------------ post kernel

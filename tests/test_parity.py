@@ -328,10 +328,11 @@ def test_persistent_repeat_and_workspace_reset():
     assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
 
 
-@pytest.mark.parametrize("T", [1, 7, 300])
+@pytest.mark.parametrize("T", [1, 7, 300, 6600])
 def test_standalone_collapse(T):
     """mhc_collapse: without the norm bit-exact to the exact-order float collapse;
-    with it within the bf16 bound of the oracle."""
+    with it within the bf16 bound of the oracle (6600 tokens: the streaming form,
+    more bytes than the memory-side cache holds)."""
     rng = np.random.default_rng(60 + T)
     d = mi.pre_inputs(T, seed=60 + T, delayed=True, norm=True)
     p = rng.uniform(0, 1, (T, 4)).astype(np.float32)
@@ -343,7 +344,7 @@ def test_standalone_collapse(T):
     check_bf16(outn, o["li_val"], o["li_mag"], what="collapse T=%d" % T)
 
 
-@pytest.mark.parametrize("T", [100, 4160])
+@pytest.mark.parametrize("T", [100, 4160, 6600])
 def test_standalone_collapse_equals_delayed_layer_input(T):
     """Without the norm, mhc_collapse(x, p) is bit-identical to the layer_input of
     mhc_pre_delayed(x, pre_in = p), on both pre-kernel forms (split and persistent)."""
