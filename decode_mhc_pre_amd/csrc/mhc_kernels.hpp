@@ -242,7 +242,9 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
 // is faster (standalone at T = 16384: 146 vs 164 us).  Same exact-order collapse
 // and folded norm; the sum of squares is taken per lane over its chunks in
 // order, then over the wave, so with the norm the two forms may differ in the
-// last bit of the norm factor.
+// last bit of the norm factor.  Its stores (layer_input, the entry seam's
+// broadcast residual) are written once and never re-read here, so they are
+// streaming (entry seam at T = 16384: 289 -> 190 us).
 constexpr int kWaveCollapseMaxC = 5120;
 template <bool kBcast>
 __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok, float p0, float p1, float p2,
@@ -278,10 +280,10 @@ __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok,
         if (kBcast) {
           // the entry seam's residual: h broadcast to the four streams, whole rows
           uint4* xo = reinterpret_cast<uint4*>(p.xout) + (size_t)tok * kNS * C8 + c8;
-          xo[0] = q[u][0];
-          xo[C8] = q[u][0];
-          xo[2 * C8] = q[u][0];
-          xo[3 * C8] = q[u][0];
+          nt_store16(q[u][0], xo);
+          nt_store16(q[u][0], xo + C8);
+          nt_store16(q[u][0], xo + 2 * C8);
+          nt_store16(q[u][0], xo + 3 * C8);
           if (p.li == nullptr) continue;
         }
         collapse8(q[u][0], q[u][1], q[u][2], q[u][3], p0, p1, p2, p3, y[ch]);
@@ -289,7 +291,7 @@ __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok,
 #pragma unroll
           for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(y[ch][e], y[ch][e], ss);
         } else {
-          lo[c8] = pack8(y[ch]);
+          nt_store16(pack8(y[ch]), lo + c8);
         }
       }
     }
@@ -305,7 +307,7 @@ __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok,
       unpack8(w8[c8], w);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (y[ch][e] * ry) * w[e];
-      lo[c8] = pack8(o);
+      nt_store16(pack8(o), lo + c8);
     }
   }
 }

@@ -194,8 +194,10 @@ def test_collapse_order_golden_on_gpu():
     assert np.all(li == 0x3F80)
 
 
-@pytest.mark.parametrize("T", [1, 16, 100])
+@pytest.mark.parametrize("T", [1, 16, 100, 2100])
 def test_broadcast_entry(T):
+    """Entry seam: split projection with per-token collapse workgroups (up to 128
+    tiles), the tile's own workgroup collapsing past that (2100 tokens)."""
     torch = torch_mod()
     d = mi.entry_inputs(T, seed=900 + T)
     h = dev_bf16(d["h"])
