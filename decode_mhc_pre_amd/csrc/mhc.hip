@@ -22,10 +22,10 @@ using namespace mhc;
 // 8.6 us against 9.1 us with 16), 16 up to 16 tiles (T = 64: 9.9 us against
 // 10.2 with 32; T = 128: 10.7 us against 12.1 with 8), 8 up to 64 tiles (T =
 // 1024: 20.7 us), 4 up to 128 (T = 2048: 34.5 us against 36.1 with 8) and 2 up
-// to 256 tiles (T = 4096: 63.9 us).  The forms that
-// collapse with their own pre-mix (mhc_pre, the entry seam) do the collapse in
-// each tile's last arriver and stop splitting past 128 tiles (T = 4096: 72 us
-// unsplit against 82 us with 2 splits).
+// to 256 tiles (T = 4096: 63.9 us).  The forms that collapse with their own
+// pre-mix (mhc_pre, the entry seam) stop splitting past 128 tiles, where each
+// tile's own workgroup collapses its tokens (T = 4096: 72 us unsplit against
+// 82 us with 2 splits).
 constexpr int kMaxSplitTiles = 256;     // tiles beyond which the row is never split
 constexpr int kMaxSplitTilesOwn = 128;  // the same for the forms with their own pre-mix
 int splits_for(int ntile, bool delayed) {
@@ -40,8 +40,8 @@ constexpr int kMaxC = 16384;
 // per-tile weight reads and duplicate residual reads (projection and collapse
 // workgroups) outweigh its parallelism.  Measured (graph replay, C = 5120):
 // delayed pre, split vs persistent, T = 1024: 21.0 vs 37.7 us, T = 4096: 63.9
-// vs 66.8 us, T = 8192: 177 vs 117 us; fused seam (post kernel + delayed split
-// kernel's fused mode vs the persistent fused kernel), T = 1281: 36.2 vs 54.9
+// vs 66.8 us, T = 8192: 177 vs 117 us; fused seam (the split kernel's fused
+// mode vs the persistent fused kernel), T = 1281: 36.2 vs 54.9
 // us, T = 2048: 55.0 vs 59.7 us, T = 3072: 79.6 vs 94.2 us, T = 4096: 135.7 vs
 // 118.3 us; delayed pre at T = 4160: 83.1 vs 73.8 us.
 constexpr int kGroupC = 5120;

@@ -319,8 +319,9 @@ __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok,
 // arriving projection workgroup has published the token's pre-mix record (the
 // four values with their sign bits set, polled with device-coherent loads and
 // cleared once read), so the collapse overlaps the projection instead of
-// following it in one workgroup per tile.  The entry seam writes its broadcast residual before
-// waiting, and does not wait at all when no layer_input is requested.
+// following it in one workgroup per tile.  The entry seam writes its broadcast
+// residual before waiting, and does not wait at all when no layer_input is
+// requested.
 // Forward progress: projection workgroups have the lower indices and are
 // dispatched first; none of them waits for anything.  The wait is bounded
 // nevertheless (kOwnWaitBudget sleeps): if it runs out the workgroup records
