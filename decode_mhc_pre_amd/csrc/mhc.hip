@@ -3,6 +3,7 @@
 // is enqueued; every launch goes to the caller's stream; nothing allocates.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -46,6 +47,13 @@ constexpr int kMaxC = 16384;
 // 118.3 us; delayed pre at T = 4160: 83.1 vs 73.8 us.
 constexpr int kGroupC = 5120;
 constexpr int kDelayedSplitMaxT = 4096;  // delayed pre: split form up to here, persistent beyond
+// Own pre-mix (mhc_pre), many tokens: the persistent kernel's gates-only form,
+// then the collapse kernel with the seam's pre-mix (a second pass over x, which
+// this form needs anyway), against the split kernel without splits (one
+// workgroup per 16-token tile collapsing its tokens after the gates): T = 4608
+// 85.7 vs 112.3 us, T = 8192 154 vs 175 us, T = 16384 292 vs 346 us (T = 3072:
+// 68.0 vs 65.1 us, T = 6144: 119.8 vs 110.5 us).
+constexpr int kOwnSplitMaxT = 4096;
 constexpr int kFusedGroupSplitMaxT = 3072;  // fused seam: the same threshold
 // Fused seam below the persistent form: the split kernel's fused mode (one
 // launch) against the post kernel followed by the delayed split kernel, T =
@@ -66,7 +74,8 @@ Plan make_plan(int T, int KB, int form, bool persist_ok) {
   pl.ntile = (T + kTileT - 1) / kTileT;
   const bool delayed = form == kModeDelayed || form == kModeFused;
   pl.persist = persist_ok && ((form == kModeDelayed && T > kDelayedSplitMaxT) ||
-                              (form == kModeFused && T > kFusedGroupSplitMaxT));
+                              (form == kModeFused && T > kFusedGroupSplitMaxT) ||
+                              (form == kModePre && T > kOwnSplitMaxT));
   int ns = pl.persist ? 1 : splits_for(pl.ntile, delayed);
   int maxs = KB / kMinKBPerSplit;
   if (maxs < 1) maxs = 1;
@@ -272,10 +281,27 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   if (pl.persist) {
     const int ng = persist_groups(T);
     if (ng > 0) {
-      if (fused)
+      if (fused) {
         hipLaunchKernelGGL((mhc_pre_persist_kernel<kGroupC, true>), dim3(ng * kPG), block, 0, s, p, ng);
-      else
+      } else if (delayed) {
         hipLaunchKernelGGL((mhc_pre_persist_kernel<kGroupC, false>), dim3(ng * kPG), block, 0, s, p, ng);
+      } else {
+        // own pre-mix: the gates, then the collapse with them (and the folded norm)
+        hipLaunchKernelGGL((mhc_pre_persist_kernel<kGroupC, false, true>), dim3(ng * kPG), block, 0, s, p, ng);
+        PreParams c{};
+        c.x = x;
+        c.pre_in = pre;
+        c.nw = norm_weight;
+        c.li = li;
+        c.eps = eps;
+        c.T = T;
+        c.C = C;
+        c.K = K;
+        if (Tz * (size_t)(n + 1) * C * 2 > kStreamBytes)
+          hipLaunchKernelGGL(mhc_collapse_kernel<true>, dim3(T), block, 0, s, c);
+        else
+          hipLaunchKernelGGL(mhc_collapse_kernel<false>, dim3(T), block, 0, s, c);
+      }
       return launched();
     }
     // a device too small for one group: the split form (its workspace need is covered)
@@ -341,7 +367,7 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
     }
   }
   // the persistent forms: fixed size
-  const int persist_min_t = (kFusedGroupSplitMaxT < kDelayedSplitMaxT ? kFusedGroupSplitMaxT : kDelayedSplitMaxT) + 1;
+  const int persist_min_t = std::min(std::min(kFusedGroupSplitMaxT, kDelayedSplitMaxT), kOwnSplitMaxT) + 1;
   if (C == kGroupC && T_max >= persist_min_t && persist_ws_bytes() > best) best = persist_ws_bytes();
   return best;
 }

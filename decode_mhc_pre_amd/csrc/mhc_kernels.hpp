@@ -872,7 +872,10 @@ struct TokenGates {
   }
 };
 
-template <int kC, bool kFused>
+// kGates: projection, exchange and gates only (no pre_in, collapse or
+// layer_input): the first of two launches for the own pre-mix form, whose
+// collapse needs this seam's gates and so follows in a second pass.
+template <int kC, bool kFused, bool kGates = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   constexpr int kCBM = kC / kKB / kPG;   // 32-column blocks per member and stream
@@ -886,6 +889,7 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   // the next unit's, consumed at step kUnit
   constexpr int kArrive = kFused ? kUnit : kPArrive;
   static_assert(kC % (kKB * kPG) == 0 && kCBM % 2 == 0, "hidden size must split into column-block pairs");
+  static_assert(!(kFused && kGates), "the gates-only form has no post stage");
   static_assert(kLd == 40 && kLd % kPQ == 0, "the exchange schedule assumes 40 loads per tile");
   static_assert(kNW * kTileT == kPT, "one 16-token MFMA tile per wave");
   __shared__ uint4 s_fnv[kLd * kFragPerKB * kWave];  // this member's weight: [stream*kCBM + block][frag][lane]
@@ -971,7 +975,8 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
 #pragma unroll
     for (int d = 0; d < kPQ; ++d) xq[d] = x_load(rx, d);
   }
-  uint4 pq = buf_load16(pin_rsrc(tile_of(0)), plane, 0);
+  uint4 pq = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (!kGates) pq = buf_load16(pin_rsrc(tile_of(0)), plane, 0);
   for (int r0 = 0; r0 < kFragRows; r0 += kNW * 10) {
     uint4 v[10];
 #pragma unroll
@@ -1221,7 +1226,7 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) y0[cb][e] = agpr_park(yw[h][e]);
         }
-      } else if (s == 0) {
+      } else if (!kGates && s == 0) {
         // the buffers move down one place, block by block, just before this
         // tile's first write of the block: tile k-1's rows are parked, tile
         // k-2's rows move to the oldest buffer
@@ -1232,11 +1237,13 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
         }
       }
       if constexpr (!kFused) {
+        if constexpr (!kGates) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ycur[cb][e] = s == 0 ? ps * f[e] : ycur[cb][e] + ps * f[e];
-        if (s == kNS - 1) {
+          for (int e = 0; e < 8; ++e) ycur[cb][e] = s == 0 ? ps * f[e] : ycur[cb][e] + ps * f[e];
+          if (s == kNS - 1) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(ycur[cb][e], ycur[cb][e], ssy);
+            for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(ycur[cb][e], ycur[cb][e], ssy);
+          }
         }
         // refill: this tile's load n + kPQ, or the next tile's first loads
         const int m = n + kPQ;
@@ -1244,7 +1251,7 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
           xq[n % kPQ] = x_load(rx, m);
         } else {
           xq[n % kPQ] = x_load(rxn, m - kLd);
-          if (m == kLd) pq = buf_load16(pin_rsrc(tnext), plane, 0);
+          if (!kGates && m == kLd) pq = buf_load16(pin_rsrc(tnext), plane, 0);
         }
       }
       // ---- exchange of tile k-1
@@ -1278,7 +1285,7 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
         constexpr int kLiStep[kCBM] = {22, 23, 24, 25, 26, 27, 28, 29, 34, 35};
 #pragma unroll
         for (int c = 0; c < kCBM; ++c)
-          if (n == kLiStep[c]) li_store(y2[c], true, ry2, rl2, c);
+          if (!kGates && n == kLiStep[c]) li_store(y2[c], true, ry2, rl2, c);
       }
       // fused refill, once the unit's raw loads are consumed (and after this
       // step's record stores): the next unit, or the next tile's first unit
@@ -1329,7 +1336,8 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
     gt.init(p, s_gv[wave], s_ba, t * kPT + wave * kTileT + mem, t >= 0);
     const rsrc_t rl = li_rsrc(t);
 #pragma unroll
-    for (int cb = 0; cb < kCBM; ++cb) li_store(yb[cb], parked, ry, rl, cb);
+    for (int cb = 0; cb < kCBM; ++cb)
+      if (!kGates) li_store(yb[cb], parked, ry, rl, cb);
     gt.finish(p);
   };
 

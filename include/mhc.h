@@ -87,8 +87,8 @@ mhc_status mhc_pack_fn(const float *fn, int K, void *fn_packed, void *stream);
 /* Workspace bytes needed by mhc_pre, mhc_pre_delayed, mhc_post_pre_delayed and
  * mhc_broadcast_entry for any T <= T_max with this n and C (few tokens: the
  * projection is split over workgroups that combine partial sums in it; with
- * C = 5120 the persistent kernels of mhc_post_pre_delayed (T > 3072) and
- * mhc_pre_delayed (T > 4096) exchange partial sums through it).  One
+ * C = 5120 the persistent kernels of mhc_post_pre_delayed (T > 3072),
+ * mhc_pre_delayed and mhc_pre (T > 4096) exchange partial sums through it).  One
  * workspace serves all of these calls.  The caller zero-fills it once after
  * allocating it; every call leaves its counters back
  * at zero, so it can be reused (and captured) without clearing. */
@@ -108,7 +108,9 @@ size_t mhc_workspace_bytes(int T_max, int n, int C);
  *   post [T][n]    float out  2*sigmoid(l[4:8]), in (0,2)
  *   comb [T][n][n] float out  Sinkhorn(exp(l[8:24])), column sums 1
  *   layer_input [T][C] bf16 out  y_c = sum_i pre_i x_{i,c}, each product
- *               rounded to float and summed over i = 0..3 left to right. */
+ *               rounded to float and summed over i = 0..3 left to right.
+ * Launches: one; with C = 5120 and T > 4096, two (the gates, then the
+ * collapse with them: the collapse needs this seam's gates). */
 mhc_status mhc_pre(const uint16_t *x, int T, int n, int C, mhc_weights w,
                    const uint16_t *norm_weight, float eps, int sinkhorn_iters,
                    float *pre, float *post, float *comb, uint16_t *layer_input,

@@ -178,11 +178,15 @@ def test_workspace_needs_by_form():
     # delayed at 4096 tokens: split form (2 splits per tile), partials in the workspace
     assert call_delayed(T=4096, ws=None) == WS
     assert call_delayed(T=4096, ws_bytes=m.mhc_workspace_bytes(4096, 4, C)) == HIP
-    # own pre-mix: split up to 128 tiles (T = 2048), beyond that one workgroup
-    # per 16-token tile, nothing to combine
+    # own pre-mix: split up to 128 tiles (T = 2048), then one workgroup per
+    # 16-token tile (nothing to combine); beyond 4096 tokens with C = 5120 the
+    # persistent gates-only form (workspace)
     assert call_pre(T=2048, ws=None) == WS
     assert call_pre(T=2049, ws=None) == HIP
     assert call_pre(T=4096, ws=None) == HIP
+    assert call_pre(T=4097, ws=None) == WS
+    assert call_pre(T=4097, ws_bytes=m.mhc_workspace_bytes(4097, 4, C)) == HIP
+    assert call_pre(T=6001, C=4096, ws=None) == HIP
 
 
 def test_valid_call_reaches_the_runtime():

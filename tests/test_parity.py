@@ -66,11 +66,13 @@ def test_pack_fn_split_and_layout():
 
 # ----------------------------------------------------------------------------- pre, delayed, entry
 
-@pytest.mark.parametrize("T", [1, 2, 7, 8, 17, 128, 1000, 2048, 2049])
+@pytest.mark.parametrize("T", [1, 2, 7, 8, 17, 128, 1000, 2048, 2049, 4097])
 def test_pre_no_norm(T):
     """Configuration 0 (T = 8, no norm) and neighbours: own pre-mix.  Up to 2048
     tokens the projection is split and one workgroup per token collapses once
-    its tile's pre-mix is published; from 2049 each tile's workgroup does it."""
+    its tile's pre-mix is published; then each tile's workgroup collapses its
+    tokens; from 4097 the persistent kernel's gates-only form runs, then the
+    collapse kernel with those gates."""
     d = mi.pre_inputs(T, seed=100 + T)
     x = dev_bf16(d["x"])
     pre, post, comb, li = M.mhc_pre(x, weights(d), None, d["eps"], d["iters"])
@@ -80,7 +82,7 @@ def test_pre_no_norm(T):
     check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="layer_input")
 
 
-@pytest.mark.parametrize("T", [1, 8, 33, 128])
+@pytest.mark.parametrize("T", [1, 8, 33, 128, 4160])
 def test_pre_with_norm(T):
     d = mi.pre_inputs(T, seed=200 + T, norm=True)
     pre, post, comb, li = M.mhc_pre(dev_bf16(d["x"]), weights(d), dev_bf16(d["norm_weight"]), d["eps"],
