@@ -253,6 +253,7 @@ def main():
         sweep = run_sweep(torch, M, mi, dev, bf, f32, w, nw)
     entry = None if args.no_sweep else run_entry(torch, M, mi, dev, bf, f32)
     collapse = None if args.no_sweep else run_collapse(torch, M, x, pre_in, nw)
+    own = None if args.no_sweep else run_own(torch, M, x, w, ws)
 
     del x, x_next, li, y
     torch.cuda.empty_cache()
@@ -291,6 +292,7 @@ def main():
         "us_per_call_sweep": sweep,
         "entry": entry,
         "collapse": collapse,
+        "pre_own": own,
         "seam_chain": chain,
     }
     print(json.dumps(line), flush=True)
@@ -395,6 +397,20 @@ def run_collapse(torch, M, x, pin, nw):
     nbytes = T * (NS * C * 2 + 16 + C * 2) + C * 2
     return {"T": T, "us": round(us, 2), "alg_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def run_own(torch, M, x, w, ws):
+    """mhc_pre (own pre-mix, no norm) on the seam's residual at T = 16384: the
+    gates-only persistent pass, then the collapse with those gates."""
+    T = x.shape[0]
+    outs = M._pre_outputs(T, C, x.device)
+    M.mhc_pre(x, w, None, 1e-6, 20, out=outs, ws=ws)
+    torch.cuda.synchronize()
+    us = _median_us(lambda n: [M.mhc_pre(x, w, None, 1e-6, 20, out=outs, ws=ws) for _ in range(n)], torch,
+                    reps=3, iters=20)
+    nbytes = pre_bytes(T, norm=False, delayed=False)
+    return {"T": T, "us": round(us, 2), "alg_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "launches": 2}
 
 
 def run_chain(torch, M, mi, dev, bf, f32, n_seams=80):
