@@ -189,6 +189,38 @@ def test_workspace_needs_by_form():
     assert call_pre(T=6001, C=4096, ws=None) == HIP
 
 
+class FarPtrs(Ptrs):
+    """Fake device addresses 16 GiB apart: no two buffers of any token count here overlap."""
+    def __call__(self, size=0):
+        p = self.next
+        self.next += 1 << 34
+        return p
+
+
+@pytest.mark.parametrize("Cx", [256, 5120, 7168])
+def test_workspace_covers_every_plan(Cx):
+    """mhc_workspace_bytes(T) is enough for every pre-stage entry point at every
+    token count up to T, whichever kernel form the call plans (split with its
+    partials, own-pre-mix records, persistent exchange): with exactly that many
+    bytes each call passes validation and reaches the runtime."""
+    lib = m.lib()
+    Ts = [1, 15, 16, 17, 32, 33, 64, 255, 256, 257, 1024, 1025, 2048, 2049, 2100, 3072, 3073,
+          4096, 4097, 6001, 16384]
+    for T_ in Ts:
+        P = FarPtrs()
+        x, h, pin, y, po, cb = P(), P(), P(), P(), P(), P()
+        w = m._Weights(P(), P(), P())
+        nw, pre, post, comb, li, xo, ws = P(), P(), P(), P(), P(), P(), P()
+        wb = m.mhc_workspace_bytes(T_, 4, Cx)
+        assert wb == 0 or wb >= m.mhc_workspace_bytes(max(T_ - 1, 1), 4, Cx)   # grows with T
+        args = (Cx, w, nw, 1e-6, 20)
+        assert lib.mhc_pre(x, T_, 4, *args, pre, post, comb, li, ws, wb, None) == HIP, ("pre", T_)
+        assert lib.mhc_pre_delayed(x, pin, T_, 4, *args, pre, post, comb, li, ws, wb, None) == HIP, ("delayed", T_)
+        assert lib.mhc_post_pre_delayed(y, x, po, cb, pin, T_, 4, *args, xo, pre, post, comb, li, ws, wb,
+                                        None) == HIP, ("fused", T_)
+        assert lib.mhc_broadcast_entry(h, T_, 4, *args, xo, pre, post, comb, li, ws, wb, None) == HIP, ("entry", T_)
+
+
 def test_valid_call_reaches_the_runtime():
     assert call_delayed() == HIP
     assert call_pre() == HIP
