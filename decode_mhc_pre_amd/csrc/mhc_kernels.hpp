@@ -957,7 +957,24 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
     return make_rsrc(rec_base + (size_t)(k >= 0 ? k % kPRing : 0) * kPRec, k >= 0 ? kPRec * 4 : 0);
   };
 
-  // ---- prologue: first x loads and pre_in, then the weight slice into LDS
+  // ---- prologue: the weight slice's loads first, then the first residual
+  // loads and pre_in, then the slice into LDS.  A wave's vector loads retire in
+  // issue order, so weight loads issued after the residual loads would each
+  // wait for those (HBM) as well.
+  constexpr int kFragPerWave = kFragRows / kNW;
+  static_assert(kFragRows % kNW == 0, "weight fragments split evenly over the waves");
+  uint4 fv[kFragPerWave];
+  {
+    const rsrc_t rf = make_rsrc(p.fnp, p.KB * kFragPerKB * kWave * 16);
+#pragma unroll
+    for (int u = 0; u < kFragPerWave; ++u) {
+      const int fr = wave + u * kNW;   // fragment row: (stream*kCBM + block)*3 + frag
+      const int lb = fr / kFragPerKB, f = fr - lb * kFragPerKB;
+      const int s = lb / kCBM, cb = lb - s * kCBM;
+      const int kbg = s * (kC / kKB) + cb0 + cb;
+      fv[u] = buf_load16(rf, ((kbg * kFragPerKB + f) * kWave + lane) * 16, 0);
+    }
+  }
   rsrc_t rx = x_rsrc(tile_of(0));
   rsrc_t ry = y_rsrc(tile_of(0));
   uint4 xq[kPQ];
@@ -977,22 +994,8 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   }
   uint4 pq = make_uint4(0u, 0u, 0u, 0u);
   if constexpr (!kGates) pq = buf_load16(pin_rsrc(tile_of(0)), plane, 0);
-  for (int r0 = 0; r0 < kFragRows; r0 += kNW * 10) {
-    uint4 v[10];
 #pragma unroll
-    for (int u = 0; u < 10; ++u) {
-      const int fr = r0 + wave + u * kNW;   // fragment row: (stream*kCBM + block)*3 + frag
-      const int lb = fr / kFragPerKB, f = fr - lb * kFragPerKB;
-      const int s = lb / kCBM, cb = lb - s * kCBM;
-      const int kbg = s * (kC / kKB) + cb0 + cb;
-      v[u] = fr < kFragRows ? p.fnp[((size_t)kbg * kFragPerKB + f) * kWave + lane] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 10; ++u) {
-      const int fr = r0 + wave + u * kNW;
-      if (fr < kFragRows) s_fnv[fr * kWave + lane] = v[u];
-    }
-  }
+  for (int u = 0; u < kFragPerWave; ++u) s_fnv[(wave + u * kNW) * kWave + lane] = fv[u];
   if (norm && tid < kCBM * 4) s_w[tid >> 2][tid & 3] = reinterpret_cast<const uint4*>(p.nw)[cb0 * 4 + tid];
   if (tid < kNL) s_ba[tid] = p.bias[tid];
   if (tid >= 32 && tid < 35) s_ba[kNL + tid - 32] = p.alpha[tid - 32];
