@@ -221,14 +221,14 @@ def main():
                     traffic=measured_traffic(key))
 
     kernels = {
-        "mhc_pre_persist_kernel<5120, true>": kentry(fused_avg, fb, "mhc_pre_persist_kernel<5120, true>"),
-        "mhc_pre_persist_kernel<5120, false>": kentry(pre_avg, pb, "mhc_pre_persist_kernel<5120, false>"),
+        "mhc_pre_persist_kernel<5120, true, false>": kentry(fused_avg, fb, "mhc_pre_persist_kernel<5120, true, false>"),
+        "mhc_pre_persist_kernel<5120, false, false>": kentry(pre_avg, pb, "mhc_pre_persist_kernel<5120, false, false>"),
         "mhc_post_kernel": kentry(post_avg, qb, "mhc_post_kernel"),
     }
     for v in kernels.values():
         v["frac"] = v["gbs"] / HBM_PEAK_GBS
     # the timed step is the fused kernel alone
-    dom = "mhc_pre_persist_kernel<5120, true>"
+    dom = "mhc_pre_persist_kernel<5120, true, false>"
     traffic = kernels[dom]["traffic"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(kernels[dom]["gbs"], 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kernels[dom]["frac"], 4),
