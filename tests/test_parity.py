@@ -299,6 +299,43 @@ def test_config2_prefill_delayed_norm_sampled():
     assert np.array_equal(li_nn, mi.f32_to_bf16_bits(y32))
 
 
+def test_prefill_own_entry_collapse_sampled():
+    """T = 16384, the launches the benchmark times for mhc_pre (the persistent
+    gates-only pass, then the streaming collapse), the entry seam and the
+    standalone collapse: GPU on all tokens, oracle on sampled rows incl. the 1%
+    outlier rows."""
+    torch = torch_mod()
+    T = 16384
+    d = mi.pre_inputs(T, seed=21, norm=True, outlier_frac=0.01)
+    rows = _sample_rows(T, d["outliers"], seed=1)
+    x = dev_bf16(d["x"])
+    pre, post, comb, li = M.mhc_pre(x, weights(d), dev_bf16(d["norm_weight"]), d["eps"], d["iters"])
+    torch.cuda.synchronize()
+    o = oracle.mhc_pre(d["x"][rows], d["fn"], d["bias"], d["alpha"], d["eps"], d["iters"],
+                       norm_weight=d["norm_weight"])
+    say("mhc_pre T=16384 sampled rows: %d" % len(rows))
+    ge = check_gates(host_f32(pre)[rows], host_f32(post)[rows], host_f32(comb)[rows], o["pre"], o["post"],
+                     o["comb"], "mhc_pre T=16384")
+    check_bf16(host_bits(li)[rows], o["li_val"], o["li_mag"], d=2 * ge, what="mhc_pre T=16384 layer_input")
+    # the standalone collapse at this size (streaming form), with the GPU's own pre-mix
+    p = host_f32(pre)
+    out = host_bits(M.mhc_collapse(x, dev_f32(p)))
+    assert np.array_equal(out[rows], mi.f32_to_bf16_bits(oracle.collapse32(d["x"][rows], p[rows])))
+    del x, pre, post, comb, li
+    # the entry seam at this size
+    e = mi.entry_inputs(T, seed=22)
+    x_out, epre, epost, ecomb, eli = M.mhc_broadcast_entry(dev_bf16(e["h"]), weights(e), dev_bf16(e["norm_weight"]),
+                                                           e["eps"], e["iters"])
+    torch.cuda.synchronize()
+    oe = oracle.mhc_broadcast_entry(e["h"][rows], e["fn"], e["bias"], e["alpha"], e["eps"], e["iters"],
+                                    norm_weight=e["norm_weight"])
+    say("entry T=16384 sampled rows: %d" % len(rows))
+    assert np.array_equal(host_bits(x_out)[rows], oe["x_out"])
+    ge = check_gates(host_f32(epre)[rows], host_f32(epost)[rows], host_f32(ecomb)[rows], oe["pre"], oe["post"],
+                     oe["comb"], "entry T=16384")
+    check_bf16(host_bits(eli)[rows], oe["li_val"], oe["li_mag"], d=2 * ge, what="entry T=16384 layer_input")
+
+
 @pytest.mark.parametrize("T", [2113, 4096, 4097, 6001])
 def test_delayed_many_tokens_every_token(T):
     """Many tokens, checked on every token: the split form with 2-4 splits per
