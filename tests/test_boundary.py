@@ -34,6 +34,26 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+RUNTIME_ALLOWED = {"hipLaunchKernel", "hipGetLastError", "hipGetDevice", "hipDeviceGetAttribute",
+                   "__hipPushCallConfiguration", "__hipPopCallConfiguration", "__hipRegisterFatBinary",
+                   "__hipRegisterFunction", "__hipUnregisterFatBinary"}
+
+
+def test_library_imports_no_allocating_or_blocking_runtime_call():
+    """Every call is capturable in a HIP graph: the library links no allocation, free,
+    memset, copy, synchronisation, module load or run-time compilation."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    so = m.lib()._name
+    out = subprocess.run(["nm", "-D", "--undefined-only", so], capture_output=True, text=True,
+                         check=True).stdout
+    used = {ln.split()[-1].split("@")[0] for ln in out.splitlines() if ln.strip()}
+    hip = {s for s in used if s.startswith(("hip", "__hip")) or "hiprtc" in s}
+    assert hip and hip <= RUNTIME_ALLOWED, sorted(hip - RUNTIME_ALLOWED)
+
+
 def test_sizes():
     assert m.mhc_fn_packed_bytes(4 * C) == 4 * C * 24 * 4
     assert m.mhc_fn_packed_bytes(0) == 0
