@@ -9,7 +9,7 @@ built, importing the ops raises.
 Entry points (same names as the C ABI):
     mhc_pack_fn, mhc_pre, mhc_pre_delayed, mhc_post, mhc_post_pre_delayed,
     mhc_broadcast_entry, mhc_collapse, mhc_workspace_bytes, mhc_fn_packed_bytes,
-    mhc_status_str
+    mhc_status_str, mhc_debug_force_wait_timeouts (test hook)
 """
 from __future__ import annotations
 
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
                   "mhc_broadcast_entry",
                   "mhc_collapse"):
             getattr(L, f).restype = I
+        L.mhc_debug_force_wait_timeouts.argtypes = [I]
+        L.mhc_debug_force_wait_timeouts.restype = I
         L.mhc_status_str.argtypes = [I]
         L.mhc_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -74,7 +76,18 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("mhc_fn_packed_bytes", "mhc_pack_fn", "mhc_workspace_bytes", "mhc_pre",
            "mhc_pre_delayed", "mhc_post", "mhc_post_pre_delayed", "mhc_broadcast_entry", "mhc_collapse",
-           "mhc_status_str")
+           "mhc_status_str", "mhc_debug_force_wait_timeouts")
+
+# Workspace byte offsets (include/mhc.h): the region calls leave zero, and the
+# words a bounded wait that ran out sets.
+WS_FLAG_BYTES = 192 * 1024
+WS_WAIT_ERROR_PERSIST = 8
+WS_WAIT_ERROR_SPLIT = 96 * 1024 + 1024
+
+
+def mhc_debug_force_wait_timeouts(sleeps: int) -> None:
+    """Test hook: sleeps > 0 makes every later wait run out after that many sleeps; 0 restores."""
+    _check(lib().mhc_debug_force_wait_timeouts(int(sleeps)), "mhc_debug_force_wait_timeouts")
 
 
 def mhc_status_str(status: int) -> str:

@@ -112,6 +112,15 @@ size_t plan_ws_bytes(const Plan& pl) {
   if (pl.nsplit <= 1) return 0;
   return kPPartOffset + (size_t)pl.ntile * pl.nsplit * kTileT * kPartStride * sizeof(float);
 }
+static_assert(MHC_WS_WAIT_ERROR_PERSIST == 2 * 4, "persistent wait-error word");
+static_assert(MHC_WS_WAIT_ERROR_SPLIT == kSplitCntOffset + kSplitWaitErr * 4, "split wait-error word");
+static_assert(MHC_WS_FLAG_BYTES == kPPartOffset, "flag region");
+
+// Bounds of the kernels' waits, set by mhc_debug_force_wait_timeouts (a
+// non-zero bias puts every wait target out of reach).
+unsigned g_wait_bias = 0;
+int g_wait_budget = kWaitBudget;
+
 void set_split_ws(PreParams& p, void* ws) {
   p.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kSplitCntOffset);
   p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + kPPartOffset);
@@ -265,6 +274,8 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   // for its tile's pre-mix (instead of the tile's last arriver collapsing all
   // of its tokens after the gates)
   p.own_wgs = (!delayed && pl.nsplit > 1 && C <= kWaveCollapseMaxC && T <= kOwnMaxTokens) ? 1 : 0;
+  p.wait_bias = g_wait_bias;
+  p.wait_budget = g_wait_budget;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 block(kThreads);
@@ -468,6 +479,13 @@ mhc_status mhc_collapse(const uint16_t* x, const float* p, int T, int n, int C,
   else
     hipLaunchKernelGGL(mhc_collapse_kernel<false>, dim3(T), dim3(kThreads), 0, s, prm);
   return launched();
+}
+
+mhc_status mhc_debug_force_wait_timeouts(int sleeps) {
+  if (sleeps < 0 || sleeps > kWaitBudget) return MHC_ERR_SHAPE;
+  g_wait_bias = sleeps ? 0x40000000u : 0u;
+  g_wait_budget = sleeps ? sleeps : kWaitBudget;
+  return MHC_OK;
 }
 
 const char* mhc_status_str(mhc_status s) {

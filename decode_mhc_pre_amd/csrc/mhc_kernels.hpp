@@ -42,6 +42,8 @@ struct PreParams {
   int T, C, K, KB;        // K = row length, KB = K / 32
   int ntile, nsplit, nproj;
   int own_wgs;            // own pre-mix: workgroups [nproj, nproj + T) collapse one token each
+  unsigned wait_bias;     // added to every wait target; non-zero makes every wait run out (tests)
+  int wait_budget;        // sleeps a bounded wait may take (per collapse workgroup / per wave)
 };
 
 constexpr int kPS = 28;      // LDS row per token: P[0..23], sum x^2 [24], sum y^2 [25]
@@ -56,7 +58,7 @@ constexpr int kSplitWaitErr = kSplitFlagStride;
 constexpr int kSplitRecBytes = 4096;
 constexpr int kOwnMaxTokens = 2048;            // tokens an own-pre-mix call with collapse workgroups may have
 constexpr int kSplitBytes = kSplitRecBytes + kOwnMaxTokens * 16;
-constexpr int kOwnWaitBudget = 1 << 20;        // sleeps per collapse workgroup (about a second)
+constexpr int kWaitBudget = 1 << 20;           // sleeps a bounded wait may take (about a second)
 constexpr unsigned kRecSet = 0x80000000u;
 constexpr int kJMax = 8;     // k-steps a wave issues together in the split kernel
 constexpr int kRedChunk = 32;  // partials loaded together by the last arriver
@@ -324,8 +326,9 @@ __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok,
 // requested.
 // Forward progress: projection workgroups have the lower indices and are
 // dispatched first; none of them waits for anything.  The wait is bounded
-// nevertheless (kOwnWaitBudget sleeps): if it runs out the workgroup records
-// it in p.cnt[kSplitWaitErr] and goes on, so the kernel always ends.
+// nevertheless (p.wait_budget sleeps): if it runs out the workgroup records
+// it in p.cnt[kSplitWaitErr] and goes on, so the kernel always ends.  A
+// non-zero p.wait_bias counts every record as missing, so each wait runs out.
 // Hidden sizes up to kWaveCollapseMaxC (3 chunks of 8 per thread).
 template <bool kBcast>
 __device__ __forceinline__ void collapse_own_token(const PreParams& p, int tok, float* s_tmp, float* s_pm) {
@@ -361,14 +364,15 @@ __device__ __forceinline__ void collapse_own_token(const PreParams& p, int tok, 
   if (tid == 0) {
     // the token's record: four words, each written with its sign bit set
     const rsrc_t rr = make_rsrc(reinterpret_cast<char*>(p.cnt) + kSplitRecBytes, p.T * 16);
-    int budget = kOwnWaitBudget;
+    int budget = p.wait_budget;
+    const bool never = p.wait_bias != 0u;
     uint4 v = buf_load16_agent(rr, tok * 16, 0);
-    while (((v.x & v.y & v.z & v.w) & kRecSet) == 0u && budget > 0) {
+    while ((never || ((v.x & v.y & v.z & v.w) & kRecSet) == 0u) && budget > 0) {
       --budget;
       __builtin_amdgcn_s_sleep(2);
       v = buf_load16_agent(rr, tok * 16, 0);
     }
-    if (((v.x & v.y & v.z & v.w) & kRecSet) == 0u) st_agent(p.cnt + kSplitWaitErr, 1u);
+    if (never || ((v.x & v.y & v.z & v.w) & kRecSet) == 0u) st_agent(p.cnt + kSplitWaitErr, 1u);
     buf_store16_agent(make_uint4(0u, 0u, 0u, 0u), rr, tok * 16, 0);   // consumed: back to empty
     s_pm[0] = __uint_as_float(v.x & ~kRecSet);
     s_pm[1] = __uint_as_float(v.y & ~kRecSet);
@@ -729,7 +733,7 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
 // Forward progress: a group is kPG consecutive blocks and blocks are dispatched
 // in order, so groups become resident whole or are preceded by groups that
 // are; those finish all their tiles and free their CUs.  The waits are bounded
-// nevertheless: a wave sleeps at most kSpinBudget times over the whole call
+// nevertheless: a wave sleeps at most p.wait_budget times over the whole call
 // (a correct call needs a few at most); if the budget runs out it records the
 // fact in workspace word 2 and stops waiting, so the kernel always ends.
 // All x, pre_in and layer_input traffic uses buffer instructions on per-tile
@@ -756,7 +760,6 @@ constexpr int kPSlots = kPRing + 1;
 constexpr size_t kPPartOffset = 192 * 1024;
 static_assert(kPCntBase * 4 + (size_t)kPMaxGroups * (kThreads / kWave) * kPSlots * kPCntStride * 4 <= kPPartOffset,
               "arrival counters overlap the records");
-constexpr int kSpinBudget = 1 << 20;  // sleeps per wave over the whole call (about a second)
 // steps of tile k at which the exchange of tiles k-1 and k-2 advances
 constexpr int kPPubA = 0;        // tile k-1: accumulators -> LDS transpose
 constexpr int kPPubB = 1;        //           LDS -> record stores
@@ -952,7 +955,10 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   float* rec_base = p.part + (size_t)(grp * kNW + wave) * kPRing * kPRec;
   // counter, arrival target and record of the group's k-th tile (k < 0: the scratch counter)
   auto cnt_of = [&](int k) { return cnt_base + (k >= 0 ? k % kPRing : kPRing) * kPCntStride; };
-  auto target_of = [&](int k) { return k >= 0 ? (unsigned)kPG * (unsigned)(k / kPRing + 1) : 0u; };
+  // (p.wait_bias, zero in a normal call, puts every target out of reach)
+  auto target_of = [&](int k) {
+    return (k >= 0 ? (unsigned)kPG * (unsigned)(k / kPRing + 1) : 0u) + p.wait_bias;
+  };
   auto rec_rsrc = [&](int k) {
     return make_rsrc(rec_base + (size_t)(k >= 0 ? k % kPRing : 0) * kPRec, k >= 0 ? kPRec * 4 : 0);
   };
@@ -1042,7 +1048,7 @@ void mhc_pre_persist_kernel(PreParams p, int ngroups) {
   };
   fetch_frags(0);
 
-  int budget = kSpinBudget;
+  int budget = p.wait_budget;
   auto wait_count = [&](const unsigned* c, unsigned target, unsigned v) {
     while ((int)(v - target) < 0 && budget > 0) {
       --budget;

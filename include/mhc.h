@@ -29,9 +29,10 @@
  *     0 <= T <= MHC_MAX_TOKENS (MHC_ERR_SHAPE otherwise).
  *   - Outputs never overlap inputs or each other (MHC_ERR_ALIAS), except the
  *     exact in-place form out == x of mhc_post.
- *   - The library keeps no state between calls.  The workspace (see
- *     mhc_workspace_bytes) is scratch for one call at a time: calls that may
- *     run concurrently need separate workspaces.
+ *   - The library keeps no state between calls (the one process-wide
+ *     setting is the test hook mhc_debug_force_wait_timeouts).  The workspace
+ *     (see mhc_workspace_bytes) is scratch for one call at a time: calls that
+ *     may run concurrently need separate workspaces.
  */
 #ifndef MHC_H
 #define MHC_H
@@ -93,6 +94,30 @@ mhc_status mhc_pack_fn(const float *fn, int K, void *fn_packed, void *stream);
  * allocating it; every call leaves its counters back
  * at zero, so it can be reused (and captured) without clearing. */
 size_t mhc_workspace_bytes(int T_max, int n, int C);
+
+/* Workspace words the calls read before they write (counters, flags and
+ * records) lie in bytes [0, MHC_WS_FLAG_BYTES); a call whose waits all
+ * completed leaves them zero.  Workgroups of one call that exchange partial
+ * sums wait for one another only in bounded waits (forward progress does not
+ * depend on the bound: a correct call on a device of its own waits a few
+ * sleeps at most).  A wait that runs out stops waiting, sets the 32-bit word
+ * at byte MHC_WS_WAIT_ERROR_PERSIST (persistent kernels) or
+ * MHC_WS_WAIT_ERROR_SPLIT (split projection) to a non-zero value and lets its
+ * kernel end.  That call's outputs are then unspecified, and the workspace
+ * must be zero-filled again before its next use. */
+#define MHC_WS_FLAG_BYTES (192 * 1024)
+#define MHC_WS_WAIT_ERROR_PERSIST 8
+#define MHC_WS_WAIT_ERROR_SPLIT (96 * 1024 + 1024)
+
+/* Test hook for the run-out path above.  sleeps > 0: every wait of later calls
+ * of mhc_pre, mhc_pre_delayed, mhc_post_pre_delayed and mhc_broadcast_entry
+ * counts as unsatisfied and is bounded by `sleeps` sleeps of 128 clocks, so
+ * each call that waits at all reports a run-out (a call whose form has no
+ * waits is unaffected).  sleeps == 0 restores the normal bound of 2^20 sleeps
+ * (about a second).  Process-wide and read when a call is enqueued; not
+ * synchronised with calls on other host threads.  MHC_ERR_SHAPE unless
+ * 0 <= sleeps <= 2^20. */
+mhc_status mhc_debug_force_wait_timeouts(int sleeps);
 
 /* Pre stage, seam collapsed with its own pre-mix (p1 Purpose: the V4 form).
  *   x           [T][n][C] bf16    residual streams.

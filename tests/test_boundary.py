@@ -299,3 +299,27 @@ def test_collapse_validation():
     assert _collapse(x, p, T, 4, C, nw, 1e-6, p) == ALIAS
     assert _collapse(x, p, 0, 4, C, nw, 1e-6, out) == OK
     assert _collapse(x, p, T, 4, C, nw, 1e-6, out) == HIP
+
+
+def test_wait_timeout_hook_validation():
+    """The test hook for bounded waits takes 0 (normal bound) to 2^20 sleeps."""
+    L = m.lib()
+    assert L.mhc_debug_force_wait_timeouts(-1) == SHAPE
+    assert L.mhc_debug_force_wait_timeouts((1 << 20) + 1) == SHAPE
+    assert L.mhc_debug_force_wait_timeouts(1 << 20) == OK
+    assert L.mhc_debug_force_wait_timeouts(0) == OK
+
+
+def test_workspace_offsets_match_header():
+    src = open(HEADER).read()
+    vals = {}
+    for name in ("MHC_WS_FLAG_BYTES", "MHC_WS_WAIT_ERROR_PERSIST", "MHC_WS_WAIT_ERROR_SPLIT"):
+        mt = re.search(r"#define\s+%s\s+(.+)" % name, src)
+        assert mt, name
+        vals[name] = eval(mt.group(1).split("/*")[0], {})
+    assert vals["MHC_WS_FLAG_BYTES"] == m.WS_FLAG_BYTES
+    assert vals["MHC_WS_WAIT_ERROR_PERSIST"] == m.WS_WAIT_ERROR_PERSIST
+    assert vals["MHC_WS_WAIT_ERROR_SPLIT"] == m.WS_WAIT_ERROR_SPLIT
+    assert max(m.WS_WAIT_ERROR_PERSIST, m.WS_WAIT_ERROR_SPLIT) + 4 <= m.WS_FLAG_BYTES
+    # every plan's workspace holds the whole flag region
+    assert m.mhc_workspace_bytes(8) >= m.WS_FLAG_BYTES
