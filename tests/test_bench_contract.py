@@ -1,0 +1,43 @@
+"""bench.py on the CPU: the one-GPU rule and the algorithmic byte counts behind its
+roofline.
+
+The byte counts are fixed by what each call must move (the seam block's inputs
+and outputs at hidden 5120, four streams, 24 logits): per token the residual
+40,960 B and layer_input 10,240 B, the gates 96 B (pre-mix, post, comb) plus the
+carried pre-mix 16 B when delayed; per call the float32 weight 1,966,080 B,
+bias and alpha 108 B and the norm weight 10,240 B; the post stage reads y and x
+and writes the next residual (92,160 B) plus its gates (80 B)."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    for n in (2, 8):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
+                           capture_output=True, text=True, cwd=ROOT, timeout=120)
+        assert r.returncode == 2, r
+        assert "one GPU only" in r.stderr
+        assert r.stdout == ""
+
+
+def test_algorithmic_bytes():
+    # own pre-mix, no norm, 8 tokens
+    assert bench.pre_bytes(8, norm=False, delayed=False) == 8 * 51_296 + 1_966_188 == 2_376_556
+    # delayed with norm: decode and prefill sizes
+    assert bench.pre_bytes(128) == 128 * 51_312 + 1_976_428 == 8_544_364
+    assert bench.pre_bytes(16384) == 842_672_236
+    # post stage
+    assert bench.post_bytes(16384) == 16384 * 92_240 == 1_511_260_160
+    # the seam as two calls, and as one: the fused call still writes the next
+    # residual (the next seam reads it) but does not read it back (40,960 B per
+    # token fewer: 143,552 -> 102,592 B per token)
+    assert bench.pre_bytes(16384) + bench.post_bytes(16384) == 2_353_932_396
+    assert bench.pre_bytes(16384) + bench.post_bytes(16384) - bench.fused_bytes(16384) == 16384 * 40_960
+    assert bench.fused_bytes(16384) == 16384 * 102_592 + 1_976_428
+    # entry: h in, four-stream residual, layer_input and gates out; the narrower weight
+    assert bench.entry_bytes(1) == 10_240 + 40_960 + 10_240 + 96 + 491_520 + 108 + 10_240
