@@ -36,6 +36,8 @@ NS = 4
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "mHC seam tokens/s at T=16384 + µs/call T=1..128; HBM GB/s as % of peak"
 SWEEP_T = (1, 2, 4, 6, 7, 8, 16, 32, 64, 128)
+S_CPU = 2048          # tokens of the seam input the CPU oracle runs (a bounded sample)
+NRMSE_T = (1, 8, 64, 1024)   # token counts of the fold-accuracy measurement (layer_input NRMSE vs fp64)
 
 
 def pre_bytes(T, C=C, norm=True, delayed=True):
@@ -150,23 +152,22 @@ def main():
     pre_in = f32(d["pre_in"])
     nw = bf(d["norm_weight"])
     w = M.make_weights(f32(d["fn"]), f32(d["bias"]), f32(d["alpha"]))
-    x_host_sample = d["x"][:4096].copy()
-    pre_in_host_sample = d["pre_in"][:4096].copy()
+    x_host_sample = d["x"][:S_CPU].copy()
     fn_h, bias_h, alpha_h, nw_h = d["fn"], d["bias"], d["alpha"], d["norm_weight"]
     del d
     # seam k's sublayer output and gates: y ~ N(0,1) bf16, gates from the library's own
     # pre stage on the same residual (real gates: post in (0,2), comb column-stochastic)
     y_h = mi.post_inputs(T_SEAM, seed=3)["y"]
     y = bf(y_h)
-    y_host_sample = y_h[:4096].copy()
+    y_host_sample = y_h[:S_CPU].copy()
     del y_h
     pre_out, post, comb, li = M._pre_outputs(T_SEAM, C, dev)
     ws = M.workspace(dev, T_SEAM, C)
     pre_k, post_k, comb_k, _ = M.mhc_pre_delayed(x, pre_in, w, nw, 1e-6, 20, ws=ws)
     x_next = torch.empty_like(x)
     torch.cuda.synchronize()
-    post_k_h, comb_k_h, pre_k_h = (post_k[:4096].cpu().numpy(), comb_k[:4096].cpu().numpy(),
-                                   pre_k[:4096].cpu().numpy())
+    post_k_h, comb_k_h, pre_k_h = (post_k[:S_CPU].cpu().numpy(), comb_k[:S_CPU].cpu().numpy(),
+                                   pre_k[:S_CPU].cpu().numpy())
     print("inputs ready in %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
@@ -215,10 +216,17 @@ def main():
         return time.perf_counter() - t_start, evs
 
     t_total, evs = timed(step, 0)
+    # a bounded wait that ran out would make the timed outputs unspecified: stop here
+    M.check_workspace(ws, clear=False)
+    fused_out_h = {"x_out": x_next[:S_CPU].view(torch.int16).cpu().numpy().view(np.uint16),
+                   "pre_out": pre_out[:S_CPU].cpu().numpy(), "post": post[:S_CPU].cpu().numpy(),
+                   "comb": comb[:S_CPU].cpu().numpy(),
+                   "li": li[:S_CPU].view(torch.int16).cpu().numpy().view(np.uint16)}
     fused_ms = [evs[0][0].elapsed_time(evs[0][1]) / args.steps]
     ms_per_step = t_total * 1e3 / args.steps
     value = T_SEAM * args.steps / t_total
     t_two, evs2 = timed(step_two, 3)
+    M.check_workspace(ws, clear=False)
     post_ms = [e[0].elapsed_time(e[1]) for e in evs2]
     pre_ms = [e[1].elapsed_time(e[2]) for e in evs2]
 
@@ -257,6 +265,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    copy = copy_ceiling(torch, dev)
+    copy["fused_frac_of_copy"] = round(kernels[dom]["gbs"] / copy["copy_GBps"], 4)
 
     # ---------------------------------------------------------------- T = 1..128 sweep
     sweep = None
@@ -270,11 +280,16 @@ def main():
     torch.cuda.empty_cache()
     chain = None if args.no_sweep else run_chain(torch, M, mi, dev, bf, f32)
 
+    M.check_default_workspaces(clear=False)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
+    accuracy = None
     if not args.no_cpu:
-        cpu = cpu_baseline(y_host_sample, x_host_sample, post_k_h, comb_k_h, pre_k_h, fn_h, bias_h, alpha_h,
-                           nw_h, args.cpu_seconds)
+        cpu, o_fused = cpu_baseline(y_host_sample, x_host_sample, post_k_h, comb_k_h, pre_k_h, fn_h, bias_h,
+                                    alpha_h, nw_h, args.cpu_seconds)
+        accuracy = oracle_accuracy(torch, M, mi, dev, bf, f32, fused_out_h, o_fused)
+        M.check_default_workspaces(clear=False)
 
     line = {
         "metric": METRIC,
@@ -287,7 +302,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16 data, fp32 accumulate, projection weight bf16 hi+lo",
         "data": "synthetic",
         "config": {"workload": "mhc seam, one launch: post of seam k + delayed pre of seam k+1 with "
                                "fused RMSNorm, T=16384, n=4, C=5120, 20 Sinkhorn iters, 1% outlier rows x100",
@@ -295,6 +310,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "accuracy": accuracy,
+        "copy_ceiling": copy,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "kernel_timing": "fused step: one HIP event pair on the launch stream around the timed launches "
@@ -490,37 +507,134 @@ def run_chain(torch, M, mi, dev, bf, f32, n_seams=80):
     return res
 
 
+def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
+    """A streaming-copy ceiling measured in the same run: the runtime's device-to-device
+    copy of 1 GiB (read + write counted), averaged over `reps` copies."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e0.record()
+    e0.synchronize()
+    ms = s0.elapsed_time(e0) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kind": "torch copy_ of 1 GiB (read + write)", "copy_GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(2 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(y, x, post_k, comb_k, pre_k, fn, bias, alpha, nw, target_s):
     """The oracle as it stands (C, OpenMP over tokens) on a bounded sample of the
-    same seam: the post stage of seam k, then the delayed pre with fused norm."""
+    same seam: the post stage of seam k, then the delayed pre with fused norm.
+    Timed on all host threads (the reported value) and on one thread, plus its
+    microseconds per call for the decode sizes T = 1..128.  Returns the baseline
+    and the oracle's result on the sample (for the accuracy figures)."""
     import oracle
     oracle.lib()
     threads = oracle.max_threads()
 
     def run(S):
         t = time.perf_counter()
-        oracle.mhc_post_pre_delayed(y[:S], x[:S], post_k[:S], comb_k[:S], pre_k[:S], fn, bias, alpha, 1e-6, 20,
-                                    norm_weight=nw)
-        return time.perf_counter() - t
+        r = oracle.mhc_post_pre_delayed(y[:S], x[:S], post_k[:S], comb_k[:S], pre_k[:S], fn, bias, alpha, 1e-6, 20,
+                                        norm_weight=nw)
+        return time.perf_counter() - t, r
 
-    S = min(len(x), 2048)
+    S = min(len(x), S_CPU)
     run(64)  # warm-up (page in, thread pool)
     reps, dt = 0, 0.0
+    res = None
     while dt < target_s and reps < 1000:
-        dt += run(S)
+        t, res = run(S)
+        dt += t
         reps += 1
-    cpu_model = ""
+    # one thread, on a smaller share of the sample (same per-token work)
+    oracle.set_threads(1)
     try:
-        with open("/proc/cpuinfo") as f:
-            for ln in f:
-                if ln.startswith("model name"):
-                    cpu_model = ln.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {"value": round(S * reps / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        S1 = 64
+        reps1, dt1 = 0, 0.0
+        while dt1 < target_s / 4 and reps1 < 100:
+            dt1 += run(S1)[0]
+            reps1 += 1
+    finally:
+        oracle.set_threads(threads)
+    # microseconds per call at the decode sizes (all threads; median of 5)
+    us = {}
+    for T in SWEEP_T:
+        ts = sorted(run(T)[0] for _ in range(5))
+        us[str(T)] = round(ts[2] * 1e6, 1)
+    base = {"value": round(S * reps / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d tokens of the T=16384 seam input (post, then pre_delayed+norm) x %d passes, "
-                      "%.1f s; %s" % (S, reps, dt, cpu_model)}
+                      "%.1f s; %s" % (S, reps, dt, _cpu_model()),
+            "one_thread_tokens_per_s": round(S1 * reps1 / dt1, 1),
+            "us_per_call": us}
+    return base, res
+
+
+def oracle_accuracy(torch, M, mi, dev, bf, f32, fused_h, o_fused):
+    """Accuracy against the oracle's float64 evaluation (the oracle leg):
+    - the benchmark's own step at T = 16384, on the first S_CPU tokens: worst
+      relative error of the gates, the next residual's bits, and layer_input NRMSE;
+    - the fold-accuracy measurement of the wavefront-fix PR (Measurements): the
+      delayed pre with the folded RMSNorm at T = 1/8/64/1024, layer_input NRMSE
+      against the exact evaluation (NRMSE = RMS(gpu - ref) / RMS(ref), with ref the
+      exact value rounded once to bf16 -- the page reports 0.0 at one token, which
+      only a rounded reference gives -- and, beside it, the unrounded value)."""
+    import oracle
+
+    def rel(g, o):
+        g = np.asarray(g, np.float64).reshape(len(g), -1)
+        o = np.asarray(o, np.float64).reshape(len(o), -1)
+        return float(np.max(np.abs(g - o) / np.abs(o)))
+
+    def nrmse(bits, exact):
+        g = oracle.bf16_to_f64(bits)
+        return float(np.sqrt(np.mean((g - exact) ** 2)) / np.sqrt(np.mean(exact ** 2)))
+
+    def nrmse_rounded(bits, exact_bits):
+        # against the exact value rounded once to bf16: 0.0 when every output is the
+        # correctly rounded one (the page's figure is 0.0 at one token)
+        return nrmse(bits, oracle.bf16_to_f64(exact_bits))
+
+    step = {"tokens": int(len(fused_h["pre_out"])),
+            "gate_max_rel_err": max(rel(fused_h["pre_out"], o_fused["pre_out"]), rel(fused_h["post"], o_fused["post"]),
+                                    rel(fused_h["comb"], o_fused["comb"])),
+            "x_out_bits_equal_single_precision_post": bool(np.array_equal(fused_h["x_out"], o_fused["x_out"])),
+            "layer_input_nrmse_vs_rounded_exact": nrmse_rounded(fused_h["li"], o_fused["li"]),
+            "layer_input_nrmse_vs_exact": nrmse(fused_h["li"], o_fused["li_val"])}
+    fold = {}
+    for T in NRMSE_T:
+        d = mi.pre_inputs(T, seed=77 + T, delayed=True, norm=True)
+        w = M.make_weights(f32(d["fn"]), f32(d["bias"]), f32(d["alpha"]))
+        pre_out, post, comb, li = M.mhc_pre_delayed(bf(d["x"]), f32(d["pre_in"]), w, bf(d["norm_weight"]), 1e-6, 20)
+        torch.cuda.synchronize()
+        o = oracle.mhc_pre_delayed(d["x"], d["pre_in"], d["fn"], d["bias"], d["alpha"], 1e-6, 20,
+                                   norm_weight=d["norm_weight"])
+        lb = li.view(torch.int16).cpu().numpy().view(np.uint16)
+        fold[str(T)] = {"layer_input_nrmse_vs_rounded_exact": nrmse_rounded(lb, o["li"]),
+                        "layer_input_nrmse_vs_exact": nrmse(lb, o["li_val"]),
+                        "gate_max_rel_err": max(rel(pre_out.cpu().numpy(), o["pre_out"]),
+                                                rel(post.cpu().numpy(), o["post"]),
+                                                rel(comb.cpu().numpy(), o["comb"]))}
+    return {"step_T16384_sample": step, "fold_delayed_norm": fold,
+            "nrmse": "RMS(gpu - ref) / RMS(ref); ref = the float64 oracle's value rounded once to bf16 "
+                     "(_vs_rounded_exact, the page's figure) or unrounded (_vs_exact, which includes the "
+                     "output's own bf16 rounding)"}
 
 
 if __name__ == "__main__":

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -127,18 +128,22 @@ void set_split_ws(PreParams& p, void* ws) {
 }
 
 // Groups of the persistent kernel: one workgroup per CU at most (its LDS use
-// guarantees that), never more groups than tiles.
-int persist_groups(int T) {
-  static int cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
+// guarantees that), never more groups than tiles.  The CU count is that of the
+// device the launch stream belongs to (not the calling thread's current
+// device), cached per device; a race between threads only stores the same
+// value twice.  -1: the device could not be queried (nothing is launched);
+// 0: fewer CUs than one group needs.
+int persist_groups(int T, hipStream_t stream) {
+  static std::atomic<int> cus[64];
+  hipDevice_t dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
   const int tiles = (T + kPT - 1) / kPT;
-  int ng = cus[dev] / kPG;
+  int ng = n / kPG;
   if (ng > kPMaxGroups) ng = kPMaxGroups;
   if (ng > tiles) ng = tiles;
   return ng;
@@ -176,7 +181,7 @@ mhc_status check_common(int T, int n, int C) {
 
 mhc_status check_scalars(float eps, int iters) {
   if (!(eps >= 0.0f) || !std::isfinite(eps)) return MHC_ERR_SHAPE;
-  if (iters < 1) return MHC_ERR_SHAPE;
+  if (iters < 1 || iters > MHC_MAX_SINKHORN_ITERS) return MHC_ERR_SHAPE;
   return MHC_OK;
 }
 
@@ -290,7 +295,8 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
     mode = kModeDelayed;
   }
   if (pl.persist) {
-    const int ng = persist_groups(T);
+    const int ng = persist_groups(T, s);
+    if (ng < 0) return MHC_ERR_HIP;
     if (ng > 0) {
       if (fused) {
         hipLaunchKernelGGL((mhc_pre_persist_kernel<kGroupC, true>), dim3(ng * kPG), block, 0, s, p, ng);

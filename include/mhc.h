@@ -47,11 +47,13 @@ extern "C" {
 #define MHC_HC_MULT 4          /* residual streams n */
 #define MHC_NUM_LOGITS 24      /* 2n + n*n: pre-mix | post | comb (row-major) */
 #define MHC_MAX_TOKENS (1 << 22)
+#define MHC_MAX_SINKHORN_ITERS 1024  /* larger iteration counts are MHC_ERR_SHAPE */
 
 typedef enum {
     MHC_OK = 0,
     MHC_ERR_NULL = 1,        /* a required pointer is NULL */
-    MHC_ERR_SHAPE = 2,       /* T < 0 or too large, eps < 0 or not finite, sinkhorn_iters < 1 */
+    MHC_ERR_SHAPE = 2,       /* T < 0 or too large, eps < 0 or not finite, sinkhorn_iters
+                                outside [1, MHC_MAX_SINKHORN_ITERS] */
     MHC_ERR_UNSUPPORTED = 3, /* n != 4, or C outside the supported set */
     MHC_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     MHC_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
@@ -103,8 +105,12 @@ size_t mhc_workspace_bytes(int T_max, int n, int C);
  * sleeps at most).  A wait that runs out stops waiting, sets the 32-bit word
  * at byte MHC_WS_WAIT_ERROR_PERSIST (persistent kernels) or
  * MHC_WS_WAIT_ERROR_SPLIT (split projection) to a non-zero value and lets its
- * kernel end.  That call's outputs are then unspecified, and the workspace
- * must be zero-filled again before its next use. */
+ * kernel end.  That call's outputs are then unspecified and must be
+ * discarded, and the workspace must be zero-filled again before its next use.
+ * The call itself still returns MHC_OK (it cannot know without waiting for
+ * the device): a caller that must not consume a wrong result reads the two
+ * words after the call's stream has drained (the Python binding's
+ * check_workspace does this and raises). */
 #define MHC_WS_FLAG_BYTES (192 * 1024)
 #define MHC_WS_WAIT_ERROR_PERSIST 8
 #define MHC_WS_WAIT_ERROR_SPLIT (96 * 1024 + 1024)
@@ -127,8 +133,9 @@ mhc_status mhc_debug_force_wait_timeouts(int sleeps);
  *                                 1/sqrt(mean(y^2) + eps), evaluated in float
  *                                 and rounded once.
  *   eps         >= 0, used in the RMS of the projection and of the norm.
- *   sinkhorn_iters >= 1 rounds of (row normalise, column normalise) on
- *               exp(comb logits) (p1 Summary: 20 iterations).
+ *   sinkhorn_iters in [1, MHC_MAX_SINKHORN_ITERS]: rounds of (row normalise,
+ *               column normalise) on exp(comb logits) (p1 Summary: 20
+ *               iterations).
  *   pre  [T][n]    float out  sigmoid(l[0:4])
  *   post [T][n]    float out  2*sigmoid(l[4:8]), in (0,2)
  *   comb [T][n][n] float out  Sinkhorn(exp(l[8:24])), column sums 1

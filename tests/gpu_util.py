@@ -79,7 +79,10 @@ def check_bf16(g_bits, val, mag, d=0.0, what=""):
     bad = err > bound
     n_bad = int(bad.sum())
     worst = float(np.max(err / bound)) if err.size else 0.0
-    say("  %s: %d values, worst err/bound %.3f, violations %d" % (what, err.size, worst, n_bad))
+    # share of outputs more than one bf16 ulp (of the exact value) away from it
+    beyond = float(np.mean(err > ulp_bf16(val))) if err.size else 0.0
+    say("  %s: %d values, worst err/bound %.3f, beyond 1 ulp %.2e, violations %d"
+        % (what, err.size, worst, beyond, n_bad))
     if n_bad:
         idx = np.argwhere(bad)[:5]
         for i in idx:

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
-RUNTIME_ALLOWED = {"hipLaunchKernel", "hipGetLastError", "hipGetDevice", "hipDeviceGetAttribute",
+RUNTIME_ALLOWED = {"hipLaunchKernel", "hipGetLastError", "hipStreamGetDevice", "hipDeviceGetAttribute",
                    "__hipPushCallConfiguration", "__hipPopCallConfiguration", "__hipRegisterFatBinary",
                    "__hipRegisterFunction", "__hipUnregisterFatBinary"}
 
@@ -52,6 +52,9 @@ def test_library_imports_no_allocating_or_blocking_runtime_call():
     used = {ln.split()[-1].split("@")[0] for ln in out.splitlines() if ln.strip()}
     hip = {s for s in used if s.startswith(("hip", "__hip")) or "hiprtc" in s}
     assert hip and hip <= RUNTIME_ALLOWED, sorted(hip - RUNTIME_ALLOWED)
+    # the persistent kernels' grid is sized from the launch stream's device, never
+    # from the calling thread's current device (which may be another GPU)
+    assert "hipStreamGetDevice" in hip and "hipGetDevice" not in hip
 
 
 def test_sizes():
@@ -136,6 +139,9 @@ def test_pre_validation(call):
     assert call(eps=float("nan")) == SHAPE
     assert call(eps=float("inf")) == SHAPE
     assert call(iters=0) == SHAPE
+    assert call(iters=1025) == SHAPE     # above MHC_MAX_SINKHORN_ITERS: rejected before any launch
+    assert call(iters=1 << 30) == SHAPE
+    assert call(iters=1024) == HIP       # the cap itself is valid (then: no GPU here)
     assert call(x=None) == NULL
     assert call(pre=None) == NULL
     assert call(comb=None) == NULL
@@ -308,6 +314,14 @@ def test_wait_timeout_hook_validation():
     assert L.mhc_debug_force_wait_timeouts((1 << 20) + 1) == SHAPE
     assert L.mhc_debug_force_wait_timeouts(1 << 20) == OK
     assert L.mhc_debug_force_wait_timeouts(0) == OK
+
+
+def test_iteration_cap_matches_header():
+    src = open(HEADER).read()
+    mt = re.search(r"#define\s+MHC_MAX_SINKHORN_ITERS\s+(\d+)", src)
+    assert mt and int(mt.group(1)) == m.MAX_SINKHORN_ITERS == 1024
+    mt = re.search(r"#define\s+MHC_MAX_TOKENS\s+\(1 << (\d+)\)", src)
+    assert mt and (1 << int(mt.group(1))) == m.MAX_TOKENS
 
 
 def test_workspace_offsets_match_header():

@@ -82,6 +82,93 @@ def test_pre_no_norm(T):
     check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="layer_input")
 
 
+def test_config0_at_its_seed():
+    """Configuration 0 exactly as stated: mhc_pre without norm, T = 8, seed 0."""
+    d = mi.pre_inputs(8, seed=0)
+    pre, post, comb, li = M.mhc_pre(dev_bf16(d["x"]), weights(d), None, d["eps"], d["iters"])
+    o = oracle.mhc_pre(d["x"], d["fn"], d["bias"], d["alpha"], d["eps"], d["iters"])
+    say("config 0 (T=8, seed 0)")
+    ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"], "cfg0")
+    check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="cfg0 layer_input")
+
+
+def _zero_rows(T):
+    return sorted({0, min(17, T - 1), T // 2, T - 1})
+
+
+@pytest.mark.parametrize("form,T", [("delayed", 40), ("delayed", 4100), ("own", 40), ("own", 4100),
+                                    ("entry", 40), ("fused", 40), ("fused", 3100)])
+def test_all_zero_rows(form, T):
+    """Tokens whose whole residual row is zero: the row's RMS is eps alone
+    (r = 1/sqrt(eps)), the logits are the bias, the collapse is zero and the folded
+    norm gives zero (0 * 1/sqrt(eps) * w).  Mixed with ordinary rows in one call,
+    on the split and the persistent forms."""
+    torch = torch_mod()
+    z = _zero_rows(T)
+    say("zero rows %s T=%d rows %s" % (form, T, z))
+    if form == "entry":
+        d = mi.entry_inputs(T, seed=1900 + T)
+        d["h"][z] = 0
+        x_out, pre, post, comb, li = M.mhc_broadcast_entry(dev_bf16(d["h"]), weights(d), dev_bf16(d["norm_weight"]),
+                                                          d["eps"], d["iters"])
+        o = oracle.mhc_broadcast_entry(d["h"], d["fn"], d["bias"], d["alpha"], d["eps"], d["iters"],
+                                       norm_weight=d["norm_weight"])
+        assert np.array_equal(host_bits(x_out), o["x_out"])
+        ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"], "entry")
+        check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="entry layer_input")
+        assert np.all(host_bits(li)[z] & 0x7FFF == 0)
+        return
+    d = mi.pre_inputs(T, seed=1950 + T, delayed=True, norm=True)
+    d["x"][z] = 0
+    if form == "own":
+        pre, post, comb, li = M.mhc_pre(dev_bf16(d["x"]), weights(d), dev_bf16(d["norm_weight"]), d["eps"],
+                                        d["iters"])
+        o = oracle.mhc_pre(d["x"], d["fn"], d["bias"], d["alpha"], d["eps"], d["iters"],
+                           norm_weight=d["norm_weight"])
+        ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"], "own")
+        li = host_bits(li)
+        check_bf16(li, o["li_val"], o["li_mag"], d=2 * ge, what="own layer_input")
+    elif form == "delayed":
+        pre_out, post, comb, li = run_delayed(d)
+        o = oracle_delayed(d)
+        check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "delayed")
+        check_bf16(li, o["li_val"], o["li_mag"], what="delayed layer_input")
+    else:
+        p, post_k, comb_k = post_gates(T, seed=1960 + T)
+        y = p["y"].copy()
+        y[z] = 0
+        got = run_fused(d, y, post_k, comb_k)
+        check_fused(got, d, y, post_k, comb_k, what="fused zero rows")
+        assert np.all(got[0][z] & 0x7FFF == 0)
+        li = got[4]
+    assert np.all(li[z] & 0x7FFF == 0)
+
+
+@pytest.mark.parametrize("form,T", [("delayed", 128), ("delayed", 4100), ("fused", 128), ("fused", 3100),
+                                    ("own", 4100)])
+@pytest.mark.parametrize("iters", [1, 7, 33])
+def test_sinkhorn_iteration_counts(form, T, iters):
+    """Iteration counts other than 20 on every kernel form (the persistent kernels
+    spread the iterations over the steps of the next tile's sweep and finish any
+    that are left when they write the gates)."""
+    d = mi.pre_inputs(T, seed=2000 + T + iters, delayed=True, norm=True)
+    d["iters"] = iters
+    say("iters=%d %s T=%d" % (iters, form, T))
+    if form == "delayed":
+        pre_out, post, comb, li = run_delayed(d)
+        o = oracle_delayed(d)
+        check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "delayed iters=%d" % iters)
+        check_bf16(li, o["li_val"], o["li_mag"], what="layer_input")
+    elif form == "own":
+        pre, post, comb, li = M.mhc_pre(dev_bf16(d["x"]), weights(d), dev_bf16(d["norm_weight"]), d["eps"], iters)
+        o = oracle.mhc_pre(d["x"], d["fn"], d["bias"], d["alpha"], d["eps"], iters, norm_weight=d["norm_weight"])
+        ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"], "own")
+        check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="own layer_input")
+    else:
+        p, post_k, comb_k = post_gates(T, seed=2100 + T)
+        check_fused(run_fused(d, p["y"], post_k, comb_k), d, p["y"], post_k, comb_k, what="fused iters=%d" % iters)
+
+
 @pytest.mark.parametrize("T", [1, 8, 33, 128, 4160])
 def test_pre_with_norm(T):
     d = mi.pre_inputs(T, seed=200 + T, norm=True)
@@ -251,6 +338,9 @@ def test_post_bits_equal_single_precision_oracle():
     p, post, comb = post_gates(T, seed=41)
     out = M.mhc_post(dev_bf16(p["y"]), dev_bf16(p["x"]), dev_f32(post), dev_f32(comb))
     assert np.array_equal(host_bits(out), oracle.post32(p["y"], p["x"], post, comb))
+    # and, independently of any order, within the bf16 bar of the exact (double) post
+    ex = oracle.mhc_post(p["y"], p["x"], post, comb)
+    check_bf16(host_bits(out), ex["out_val"], ex["out_mag"], what="post vs exact")
     yb = np.full((1, C), 0x3F80, np.uint16)
     xb = np.full((1, 4, C), 0x3F80, np.uint16)
     pp = np.float32([[1.0 + 2.0 ** -8, 0, 0, 0]])
@@ -629,7 +719,100 @@ def test_config4_seam_chain(T):
     assert worst <= CHAIN_GATE_RTOL and rel <= CHAIN_X_RTOL
 
 
+@pytest.mark.parametrize("T", [2048, 16384])
+def test_config4_seam_chain_sampled(T):
+    """Configuration 4 at the sizes the benchmark's chain reports beyond the decode
+    sizes: T = 2048 (the split kernel's fused mode) and T = 16384 (the persistent
+    fused kernel).  The GPU chain runs on all T tokens.  The oracle chain follows
+    32 sampled token rows through the entry seam and all 80 seams (tokens are
+    independent, so a row's chain does not depend on the others).  At every seam the
+    GPU also runs one full-size launch on a copy of its own state in which the
+    sampled rows are replaced by the oracle chain's values, and those rows are held
+    to the tight per-seam bars against the oracle's next seam; the free-running GPU
+    chain is held to the drift bounds of the small-T chain test."""
+    torch = torch_mod()
+    n_seams = 80
+    rng = np.random.default_rng(T)
+    rows = np.array(sorted({0, T - 1} | set(rng.choice(T, 30, replace=False).tolist())))
+    idx = torch.from_numpy(rows).cuda()
+    e = mi.entry_inputs(T, seed=999)
+    sws = _chain_weights(n_seams, C)
+    gw = [M.make_weights(dev_f32(sw["fn"]), dev_f32(sw["bias"]), dev_f32(sw["alpha"])) for sw in sws]
+    gnw = [dev_bf16(sw["norm_weight"]) for sw in sws]
+    we = M.make_weights(dev_f32(e["fn"]), dev_f32(e["bias"]), dev_f32(e["alpha"]))
+    say("config 4 sampled T=%d: entry" % T)
+    x, pre, post, comb, li = M.mhc_broadcast_entry(dev_bf16(e["h"]), we, dev_bf16(e["norm_weight"]), e["eps"],
+                                                   e["iters"])
+    o = oracle.mhc_broadcast_entry(e["h"][rows], e["fn"], e["bias"], e["alpha"], e["eps"], e["iters"],
+                                   norm_weight=e["norm_weight"])
+    assert np.array_equal(host_bits(x.index_select(0, idx)), o["x_out"])
+    ox, opre, opost, ocomb, oli = o["x_out"], o["pre"], o["post"], o["comb"], o["li"]
+    xs = torch.empty_like(x)
+    worst = 0.0
+    for k in range(n_seams):
+        sw = sws[k]
+        p32, c32, q32 = opost.astype(np.float32), ocomb.astype(np.float32), opre.astype(np.float32)
+        f = oracle.mhc_post_pre_delayed(oli, ox, p32, c32, q32, sw["fn"], sw["bias"], sw["alpha"], 1e-6, 20,
+                                        norm_weight=sw["norm_weight"])
+        # one full-size launch with the oracle chain's rows scattered into the GPU state
+        xc, lic = x.clone(), li.clone()
+        prec, postc, combc = pre.clone(), post.clone(), comb.clone()
+        xc.index_copy_(0, idx, dev_bf16(ox))
+        lic.index_copy_(0, idx, dev_bf16(oli))
+        prec.index_copy_(0, idx, dev_f32(q32))
+        postc.index_copy_(0, idx, dev_f32(p32))
+        combc.index_copy_(0, idx, dev_f32(c32))
+        outs = M._pre_outputs(T, C, x.device)
+        M.mhc_post_pre_delayed(lic, xc, postc, combc, prec, gw[k], gnw[k], 1e-6, 20, out=(xs,) + tuple(outs))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(xs.index_select(0, idx)), f["x_out"]), k
+        check_gates(host_f32(outs[0].index_select(0, idx)), host_f32(outs[1].index_select(0, idx)),
+                    host_f32(outs[2].index_select(0, idx)), f["pre_out"], f["post"], f["comb"], "seam %d" % k)
+        check_bf16(host_bits(outs[3].index_select(0, idx)), f["li_val"], f["li_mag"], what="seam %d layer_input" % k)
+        del xc, lic, prec, postc, combc, outs
+        # the free-running chain advances on its own outputs
+        x, pre, post, comb, li = M.mhc_post_pre_delayed(li, x, post, comb, pre, gw[k], gnw[k], 1e-6, 20)
+        ox, opre, opost, ocomb, oli = f["x_out"], f["pre_out"], f["post"], f["comb"], f["li"]
+        errs = (rel_err(host_f32(pre.index_select(0, idx)), opre), rel_err(host_f32(post.index_select(0, idx)), opost),
+                rel_err(host_f32(comb.index_select(0, idx)).reshape(-1, 16), ocomb.reshape(-1, 16)))
+        worst = max(worst, max(errs))
+    x_final = M.mhc_post(li, x, post, comb)
+    torch.cuda.synchronize()
+    gxf = oracle.bf16_to_f64(host_bits(x_final.index_select(0, idx)))
+    oxf = oracle.bf16_to_f64(oracle.post32(oli, ox, opost.astype(np.float32), ocomb.astype(np.float32)))
+    rel = np.linalg.norm(gxf - oxf) / np.linalg.norm(oxf)
+    say("config 4 T=%d sampled: free chain worst gate rel err over 80 seams %.2e, final residual rel L2 err %.2e"
+        % (T, worst, rel))
+    assert worst <= CHAIN_GATE_RTOL and rel <= CHAIN_X_RTOL
+
+
 # ----------------------------------------------------------------------------- other hidden sizes
+
+@pytest.mark.parametrize("Cx,T", [(7168, 4100), (4096, 3100), (4096, 4100)])
+def test_other_hidden_sizes_many_tokens(Cx, T):
+    """Other hidden sizes at token counts past the decode sizes, every token: the
+    fused seam (its x_out bit for bit equal to mhc_post's), the delayed pre and the
+    own pre-mix form against the oracle."""
+    torch = torch_mod()
+    d = mi.pre_inputs(T, seed=2200 + Cx + T, C=Cx, delayed=True, norm=True, outlier_frac=0.01)
+    say("hidden %d T=%d" % (Cx, T))
+    p, post_k, comb_k = post_gates(T, seed=2300 + T)
+    y = mi.post_inputs(T, seed=2301, C=Cx)["y"]
+    got = run_fused(d, y, post_k, comb_k)
+    check_fused(got, d, y, post_k, comb_k, what="fused C=%d T=%d" % (Cx, T))
+    xo = M.mhc_post(dev_bf16(y), dev_bf16(d["x"]), dev_f32(post_k), dev_f32(comb_k))
+    torch.cuda.synchronize()
+    assert np.array_equal(got[0], host_bits(xo))
+    del xo
+    pre_out, post, comb, li = run_delayed(d)
+    o = oracle_delayed(d)
+    check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "delayed C=%d" % Cx)
+    check_bf16(li, o["li_val"], o["li_mag"], what="delayed layer_input")
+    pre, post, comb, li = M.mhc_pre(dev_bf16(d["x"]), weights(d), dev_bf16(d["norm_weight"]), d["eps"], d["iters"])
+    o = oracle.mhc_pre(d["x"], d["fn"], d["bias"], d["alpha"], d["eps"], d["iters"], norm_weight=d["norm_weight"])
+    ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"], "own C=%d" % Cx)
+    check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="own layer_input")
+
 
 @pytest.mark.parametrize("Cx,T", [(256, 1), (256, 300), (1024, 37), (7168, 5), (7168, 300), (16384, 37)])
 def test_other_hidden_sizes(Cx, T):
