@@ -46,7 +46,16 @@ constexpr int kMaxC = 16384;
 // mode vs the persistent fused kernel), T = 1281: 36.2 vs 54.9
 // us, T = 2048: 55.0 vs 59.7 us, T = 3072: 79.6 vs 94.2 us, T = 4096: 135.7 vs
 // 118.3 us; delayed pre at T = 4160: 83.1 vs 73.8 us.
-constexpr int kGroupC = 5120;
+// Hidden sizes with a persistent form, and the workgroups of one group (the
+// member count: each member's weight slice must fit in LDS).
+int persist_pg(int C) {
+  switch (C) {
+    case 4096: return PersistGeom<4096>::kPG;
+    case 5120: return PersistGeom<5120>::kPG;
+    case 7168: return PersistGeom<7168>::kPG;
+    default: return 0;
+  }
+}
 constexpr int kDelayedSplitMaxT = 4096;  // delayed pre: split form up to here, persistent beyond
 // Own pre-mix (mhc_pre), many tokens: the persistent kernel's gates-only form,
 // then the collapse kernel with the seam's pre-mix (a second pass over x, which
@@ -65,13 +74,16 @@ constexpr int kFusedSplitMaxT = 3072;
 
 struct Plan {
   int ntile, nsplit, nproj;
-  bool persist;  // persistent delayed form (C = 5120, many tokens)
+  bool persist;  // persistent form (C with a persistent geometry, many tokens)
+  int pg;        // its group size
 };
 
 // form: kModePre / kModeEntry (own pre-mix), kModeDelayed or kModeFused;
-// persist_ok: the persistent kernels exist for this hidden size.
-Plan make_plan(int T, int KB, int form, bool persist_ok) {
+// pg: group size of the persistent kernels for this hidden size (0: none).
+Plan make_plan(int T, int KB, int form, int pg) {
   Plan pl;
+  const bool persist_ok = pg > 0;
+  pl.pg = pg;
   pl.ntile = (T + kTileT - 1) / kTileT;
   const bool delayed = form == kModeDelayed || form == kModeFused;
   pl.persist = persist_ok && ((form == kModeDelayed && T > kDelayedSplitMaxT) ||
@@ -106,10 +118,10 @@ static_assert((kSplitFlagStride + 1) * sizeof(unsigned) <= (size_t)kSplitRecByte
               "split counters overlap the own-pre-mix records");
 static_assert(kMaxSplitTilesOwn * kTileT <= kOwnMaxTokens, "own-pre-mix records too few for a split call");
 static_assert(kSplitCntOffset + kSplitBytes <= kPPartOffset, "split counters and records overlap the data region");
-static_assert(kPCntBase * 4 + (size_t)kPMaxGroups * 4 * kPSlots * kPCntStride * 4 <= kSplitCntOffset,
+static_assert(kPCntBase * 4 + (size_t)kPMaxGroups * kPW * kPSlots * kPCntStride * 4 <= kSplitCntOffset,
               "persistent counters overlap the split counters");
 size_t plan_ws_bytes(const Plan& pl) {
-  if (pl.persist) return persist_ws_bytes();
+  if (pl.persist) return persist_ws_bytes(pl.pg);
   if (pl.nsplit <= 1) return 0;
   return kPPartOffset + (size_t)pl.ntile * pl.nsplit * kTileT * kPartStride * sizeof(float);
 }
@@ -133,7 +145,7 @@ void set_split_ws(PreParams& p, void* ws) {
 // device), cached per device; a race between threads only stores the same
 // value twice.  -1: the device could not be queried (nothing is launched);
 // 0: fewer CUs than one group needs.
-int persist_groups(int T, hipStream_t stream) {
+int persist_groups(int T, int pg, hipStream_t stream) {
   static std::atomic<int> cus[64];
   hipDevice_t dev = 0;
   if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
@@ -143,7 +155,7 @@ int persist_groups(int T, hipStream_t stream) {
     cus[dev].store(n, std::memory_order_relaxed);
   }
   const int tiles = (T + kPT - 1) / kPT;
-  int ng = n / kPG;
+  int ng = n / pg;
   if (ng > kPMaxGroups) ng = kPMaxGroups;
   if (ng > tiles) ng = tiles;
   return ng;
@@ -188,6 +200,19 @@ mhc_status check_scalars(float eps, int iters) {
 mhc_status launched() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? MHC_OK : MHC_ERR_HIP;
+}
+
+// The persistent kernel of hidden size kC in the form `mode` (fused seam,
+// delayed pre, or the gates-only pass of the own-pre-mix form).
+template <int kC>
+void launch_persist(int mode, const PreParams& p, int ng, hipStream_t s) {
+  const dim3 grid(ng * PersistGeom<kC>::kPG), block(kPThreads);
+  if (mode == kModeFused)
+    hipLaunchKernelGGL((mhc_persist_kernel<kC, true>), grid, block, 0, s, p, ng);
+  else if (mode == kModeDelayed)
+    hipLaunchKernelGGL((mhc_persist_kernel<kC, false>), grid, block, 0, s, p, ng);
+  else
+    hipLaunchKernelGGL((mhc_persist_kernel<kC, false, true>), grid, block, 0, s, p, ng);
 }
 
 // The previous seam's post-stage inputs of the fused form.
@@ -239,7 +264,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   if (any_alias(outs, 6, ins, 9)) return MHC_ERR_ALIAS;
 
   if (T == 0) return MHC_OK;
-  Plan pl = make_plan(T, KB, mode, C == kGroupC);
+  Plan pl = make_plan(T, KB, mode, entry ? 0 : persist_pg(C));
   const size_t need = plan_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return MHC_ERR_WORKSPACE;
 
@@ -295,16 +320,16 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
     mode = kModeDelayed;
   }
   if (pl.persist) {
-    const int ng = persist_groups(T, s);
+    const int ng = persist_groups(T, pl.pg, s);
     if (ng < 0) return MHC_ERR_HIP;
     if (ng > 0) {
-      if (fused) {
-        hipLaunchKernelGGL((mhc_pre_persist_kernel<kGroupC, true>), dim3(ng * kPG), block, 0, s, p, ng);
-      } else if (delayed) {
-        hipLaunchKernelGGL((mhc_pre_persist_kernel<kGroupC, false>), dim3(ng * kPG), block, 0, s, p, ng);
-      } else {
-        // own pre-mix: the gates, then the collapse with them (and the folded norm)
-        hipLaunchKernelGGL((mhc_pre_persist_kernel<kGroupC, false, true>), dim3(ng * kPG), block, 0, s, p, ng);
+      switch (C) {
+        case 4096: launch_persist<4096>(mode, p, ng, s); break;
+        case 5120: launch_persist<5120>(mode, p, ng, s); break;
+        default: launch_persist<7168>(mode, p, ng, s); break;
+      }
+      if (mode == kModePre) {
+        // own pre-mix: the gates above, then the collapse with them (and the folded norm)
         PreParams c{};
         c.x = x;
         c.pre_in = pre;
@@ -322,7 +347,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
       return launched();
     }
     // a device too small for one group: the split form (its workspace need is covered)
-    pl = make_plan(T, KB, mode, false);
+    pl = make_plan(T, KB, mode, 0);
     p.ntile = pl.ntile;
     p.nsplit = pl.nsplit;
     p.nproj = pl.nproj;
@@ -377,7 +402,7 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
   for (int KB : KBs) {
     for (int nt = 1; nt <= ntile_max && nt <= kMaxSplitTiles; ++nt) {
       for (int form : {kModePre, kModeDelayed, kModeFused}) {
-        const Plan pl = make_plan(nt * kTileT, KB, form, false);
+        const Plan pl = make_plan(nt * kTileT, KB, form, 0);
         const size_t b = plan_ws_bytes(pl);
         if (b > best) best = b;
       }
@@ -385,7 +410,8 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
   }
   // the persistent forms: fixed size
   const int persist_min_t = std::min(std::min(kFusedGroupSplitMaxT, kDelayedSplitMaxT), kOwnSplitMaxT) + 1;
-  if (C == kGroupC && T_max >= persist_min_t && persist_ws_bytes() > best) best = persist_ws_bytes();
+  const int pg = persist_pg(C);
+  if (pg > 0 && T_max >= persist_min_t && persist_ws_bytes(pg) > best) best = persist_ws_bytes(pg);
   return best;
 }
 

@@ -193,6 +193,35 @@ __device__ __forceinline__ uint4 post_stream8(float pw, float c0, float c1, floa
   return pack8(o);
 }
 
+// One stream of the post stage from packed inputs (the same operations and
+// order as post_stream8): only the five inputs' packed words and this
+// stream's gates are live, at the price of unpacking the inputs per stream.
+__device__ __forceinline__ uint4 post_packed8(float pw, float c0, float c1, float c2, float c3, const uint4& yv,
+                                             const uint4& v0, const uint4& v1, const uint4& v2,
+                                             const uint4& v3) {
+  uint32_t o[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const uint32_t yw = h == 0 ? yv.x : h == 1 ? yv.y : h == 2 ? yv.z : yv.w;
+    const uint32_t w0 = h == 0 ? v0.x : h == 1 ? v0.y : h == 2 ? v0.z : v0.w;
+    const uint32_t w1 = h == 0 ? v1.x : h == 1 ? v1.y : h == 2 ? v1.z : v1.w;
+    const uint32_t w2 = h == 0 ? v2.x : h == 1 ? v2.y : h == 2 ? v2.z : v2.w;
+    const uint32_t w3 = h == 0 ? v3.x : h == 1 ? v3.y : h == 2 ? v3.z : v3.w;
+    float r[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float a = pw * (b ? bf_odd(yw) : bf_even(yw));
+      a = __builtin_fmaf(c0, b ? bf_odd(w0) : bf_even(w0), a);
+      a = __builtin_fmaf(c1, b ? bf_odd(w1) : bf_even(w1), a);
+      a = __builtin_fmaf(c2, b ? bf_odd(w2) : bf_even(w2), a);
+      a = __builtin_fmaf(c3, b ? bf_odd(w3) : bf_even(w3), a);
+      r[b] = a;
+    }
+    o[h] = pack2(r[0], r[1]);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // ---------------------------------------------------------------- reductions
 // Butterfly over all 64 lanes: every lane ends with the same bits (float
 // addition is commutative, so partner lanes form identical sums).

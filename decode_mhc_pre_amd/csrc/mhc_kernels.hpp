@@ -5,11 +5,12 @@
 //                               workgroups (few tokens) or one workgroup per
 //                               16-token tile, last-arriver reduction, gates +
 //                               Sinkhorn, collapse + folded RMSNorm.
-//   mhc_pre_persist_kernel      delayed pre stage for many tokens (C = 5120):
-//                               persistent groups of 16 workgroups, one sweep
-//                               over x per 64-token tile; projection (weight
-//                               slice resident in LDS), both sums of squares,
-//                               collapse and norm fused.
+//   mhc_persist_kernel          (mhc_persist.hpp) pre stage for many tokens at
+//                               C = 4096, 5120, 7168: persistent groups of
+//                               workgroups, one sweep over x per 64-token tile;
+//                               projection (weight slice resident in LDS), both
+//                               sums of squares, collapse and norm fused; the
+//                               fused seam and the gates-only pass as variants.
 //   mhc_collapse_kernel         standalone collapse (+ folded norm), one token per workgroup.
 //   mhc_post_kernel             post stage: post_i * y + sum_j comb_ij x_j.
 #pragma once
@@ -669,711 +670,10 @@ __global__ __launch_bounds__(256) void mhc_pre_split_kernel(PreParams p) {
   }
 }
 
-// ------------------------------------------------------------------ pre kernel, persistent delayed form
-// Many tokens, hidden size fixed at compile time.  Tokens are cut into tiles
-// of 64; a group of kPG workgroups covers one tile at a time, member r owning
-// hidden columns [r*C/kPG, (r+1)*C/kPG) of all four streams, wave w owning
-// tokens 16w..16w+15.  The grid is persistent: group j walks tiles j,
-// j + ngroups, ...; a member's column range never changes, so its slice of
-// the packed projection weight (40 k-blocks, 120 KB) is copied into LDS once
-// and every MFMA B operand afterwards comes from LDS.
-//
-// Per tile a wave issues 40 loads of 16 B per lane (the MFMA A operand: 16
-// tokens x 8 columns), ordered so that two consecutive loads cover one full
-// 128-byte line of each token row, and keeps kPQ of them in flight; the queue
-// runs on into the next tile without a break.  Each load feeds, without being
-// re-read:
-//   - the partial projection (3 MFMAs against the LDS weight fragments),
-//   - the partial row sum of squares (MFMA of the fragment with itself: its
-//     diagonal holds the per-token sums),
-//   - one step of the exact-order collapse with the carried pre-mix
-//     (y = fl(fl(fl(fl(p0 x0) + fl(p1 x1)) + fl(p2 x2)) + fl(p3 x3)), each
-//     load adding one stream's product),
-//   - after the last stream of a column block, the partial sum of squares of
-//     the collapsed row (folded RMSNorm).
-// The collapsed rows of a tile stay in registers until the norm factor is
-// known: three buffers, the current tile's and the two before it.
-//
-// Exchange.  Each wave is in a group of 16 waves, the ones with its index in
-// the 16 members, sharing the same 16 tokens.  Its record per tile holds a
-// 1 KB block of row sums of squares of the collapsed rows, [member][token],
-// and a 32 KB block of the other 25 partial sums, [token][member][32] (24
-// projections and the row sum of squares of x, padded to a 128-byte line),
-// so that every store and load of the exchange moves whole lines: a member
-// writes 64 bytes and 2 KB, a reader loads 1 KB and its gate token's 2 KB.
-// A tile's partial sums leave the MFMA accumulators at the end of its sweep;
-// everything after that runs inside the next two sweeps, at fixed steps, so
-// that the x queue never drains.  During tile k + 1:
-//   steps 0-1:    store tile k's partial sums into record slot k % 4 (through
-//                 this wave's LDS transpose), without waiting;
-//   step 10:      increment slot k's arrival counter, once the first x load
-//                 issued after those stores has returned (vector memory
-//                 operations of a wave complete in issue order, so the stores
-//                 are complete as well).
-// During tile k + 2, a whole tile after every member's arrival:
-//   step 4:       read the counter; step 12: check it (a wait here means a
-//                 member is a tile behind) and load the group's records;
-//   steps 19-21:  records through LDS; norm factors of the 16 tokens (every
-//                 member sums the members' partials in the same fixed order,
-//                 so all hold the same bits); the gate token's sums;
-//   steps 22-24:  gates of one token (member r takes token r), then one
-//                 Sinkhorn iteration per step, written at step 5 of the next
-//                 tile;
-//   steps 22-35:  the wave's columns of layer_input of tile k, one 32-column
-//                 block per step, from the oldest buffer.
-// The three row buffers move down one place block by block during a sweep,
-// just before the block's first write (parked buffers live in the AGPRs).
-// Slot k % 4 is rewritten during tile k + 5, after the writer checked (at step
-// 12 of tile k + 4) that every member arrived for tile k + 2, which each does
-// in tile k + 3, after consuming tile k's records in tile k + 2.
-// Counters only grow within a call (target = kPG x uses of the slot); the
-// last wave of the grid to finish sets them back to zero, so the workspace is
-// left as found.
-//
-// Forward progress: a group is kPG consecutive blocks and blocks are dispatched
-// in order, so groups become resident whole or are preceded by groups that
-// are; those finish all their tiles and free their CUs.  The waits are bounded
-// nevertheless: a wave sleeps at most p.wait_budget times over the whole call
-// (a correct call needs a few at most); if the budget runs out it records the
-// fact in workspace word 2 and stops waiting, so the kernel always ends.
-// All x, pre_in and layer_input traffic uses buffer instructions on per-tile
-// descriptors: rows past the last token of a ragged tile read as zero and
-// their stores are dropped by the range check; a descriptor of zero bytes
-// stands for "no such tile", so the first and last tiles need no branches.
-constexpr int kPG = 16;          // members (workgroups) per tile group
-constexpr int kPT = 64;          // tokens per tile, 16 per wave
-constexpr int kPQ = 8;           // x loads in flight per wave
-constexpr int kPMaxGroups = 16;  // at most 256 workgroups; the workspace is sized for this many groups
-constexpr int kPVals = 25;       // exchanged per token besides sum y^2: P[24], sum x^2
-constexpr int kPLine = 32;       // floats per (token, member) in the value block: one 128-byte line
-constexpr int kPSsy = kPG * kTileT;                    // floats of the sum-y^2 block
-constexpr int kPRec = kPSsy + kTileT * kPG * kPLine;   // floats per (group, wave, slot)
-constexpr int kPRing = 4;        // record slots per (group, wave)
-// Workspace: word 0 counts finished waves, word 2 flags a wait that ran out of
-// budget; arrival counters from word kPCntBase, one per (group, wave, slot)
-// plus a scratch one (slot kPRing) for the first tile, each alone in its own
-// 256-byte block (packed together, the chip's polls would all land on one
-// memory channel); records from byte kPPartOffset.
-constexpr int kPCntBase = 64;
-constexpr int kPCntStride = 64;  // words
-constexpr int kPSlots = kPRing + 1;
-constexpr size_t kPPartOffset = 192 * 1024;
-static_assert(kPCntBase * 4 + (size_t)kPMaxGroups * (kThreads / kWave) * kPSlots * kPCntStride * 4 <= kPPartOffset,
-              "arrival counters overlap the records");
-// steps of tile k at which the exchange of tiles k-1 and k-2 advances
-constexpr int kPPubA = 0;        // tile k-1: accumulators -> LDS transpose
-constexpr int kPPubB = 1;        //           LDS -> record stores
-constexpr int kPArrive = 10;     //           arrival (load 10 is the first issued after the stores)
-constexpr int kPCnt = 4;         // tile k-2: read the counter
-constexpr int kPCheck = 12;      //           check it, load the records
-constexpr int kPStage = 19;      //           records -> LDS
-constexpr int kPSumY = 20;       //           norm factors
-constexpr int kPSumG = 21;       //           the gate token's sums
-constexpr int kPInit = 22;       //           gates: logits, exponentials, sigmoids (3 steps)
-constexpr int kPIter = kPInit + 3;   //       Sinkhorn iterations from here, one per step
-constexpr int kPGateEnd = kPIter + 20 - 40;   // step of the following tile at which the gates are written
-
-inline size_t persist_ws_bytes() {
-  return kPPartOffset + (size_t)kPMaxGroups * kNS * kPRing * kPRec * sizeof(float);
-}
-
-// Partial sums cross workgroups (and XCDs) through device-coherent accesses:
-// agent-scope atomic stores and loads, each coherent on its own, so no release
-// fence has to write back the L2.
-constexpr int kWaitVmem0 = 0x0f70;   // s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained (gfx9 encoding)
-// The accumulation registers (AGPRs) as parking space for values that wait a
-// tile or two: keeps the architectural registers free for the load queue.
-__device__ __forceinline__ float agpr_park(float v) {
-  float a;
-  __asm__("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
-  return a;
-}
-__device__ __forceinline__ float agpr_move(float a) {
-  float b;
-  __asm__("v_accvgpr_mov_b32 %0, %1" : "=a"(b) : "a"(a));
-  return b;
-}
-__device__ __forceinline__ float agpr_read(float a) {
-  float v;
-  __asm__("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
-  return v;
-}
-
-// An opaque zero that the compiler cannot compute before `v` is in a register:
-// whatever uses it waits for the load that produced `v`.
-__device__ __forceinline__ unsigned zero_after(unsigned v) {
-  unsigned z;
-  __asm__ volatile("v_and_b32 %0, 0, %1" : "=v"(z) : "v"(v));
-  return z;
-}
-
-// Gates and Sinkhorn of one token, in pieces.  The token's 25 summed values
-// (P[24], sum x^2) sit in `v`; `ba` holds bias[24] then alpha[3] (both LDS:
-// no global load here, whose wait would also wait for every x load in
-// flight).  Every quad of the wave computes the same token (lane & 3 = comb
-// row); quad 0 writes.  The same gates and Sinkhorn as tile_gates, one comb
-// row per lane.
-struct TokenGates {
-  float m[4];
-  float pr, po;
-  int tok, it;
-  bool write;
-
-  // in three pieces (each a short dependent chain): logits, exponentials, gates
-  __device__ __forceinline__ void init_a(const PreParams& p, const float* v, const float* ba, int t,
-                                         bool w) {
-    const int row = threadIdx.x & 3;
-    const float r = 1.0f / sqrtf(v[24] / (float)p.K + p.eps);
-    const float ac = ba[kNL + 2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] = ac * (r * v[8 + 4 * row + j]) + ba[8 + 4 * row + j];
-    pr = ba[kNL] * (r * v[row]) + ba[row];          // the pre logit, until init_c
-    po = ba[kNL + 1] * (r * v[4 + row]) + ba[4 + row];
-    tok = t;
-    it = 0;
-    write = w;
-  }
-  __device__ __forceinline__ void init_b() {
-    const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] = expf(m[j] - mx);
-  }
-  __device__ __forceinline__ void init_c() {
-    pr = 1.0f / (1.0f + expf(-pr));
-    po = 2.0f / (1.0f + expf(-po));
-  }
-  __device__ __forceinline__ void init(const PreParams& p, const float* v, const float* ba, int t,
-                                       bool w) {
-    init_a(p, v, ba, t, w);
-    init_b();
-    init_c();
-  }
-  __device__ __forceinline__ void step(int iters) {   // one Sinkhorn iteration, if any are left
-    if (it < iters) {
-      const float inv = __builtin_amdgcn_rcpf((m[0] + m[1]) + (m[2] + m[3]));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) m[j] *= inv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float c = m[j] + dpp_quad_xor1(m[j]);
-        c = c + dpp_quad_xor2(c);
-        m[j] *= __builtin_amdgcn_rcpf(c);
-      }
-      ++it;
-    }
-  }
-  __device__ __forceinline__ void finish(const PreParams& p) {
-    while (it < p.iters) step(p.iters);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int row = lane & 3;
-    if (write && lane < 4 && tok < p.T) {
-      reinterpret_cast<float4*>(p.comb)[(size_t)tok * 4 + row] = make_float4(m[0], m[1], m[2], m[3]);
-      p.pre[(size_t)tok * kNS + row] = pr;
-      p.post[(size_t)tok * kNS + row] = po;
-    }
-    write = false;
-  }
-};
-
-// kGates: projection, exchange and gates only (no pre_in, collapse or
-// layer_input): the first of two launches for the own pre-mix form, whose
-// collapse needs this seam's gates and so follows in a second pass.
-template <int kC, bool kFused, bool kGates = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mhc_pre_persist_kernel(PreParams p, int ngroups) {
-  constexpr int kCBM = kC / kKB / kPG;   // 32-column blocks per member and stream
-  constexpr int kLd = kNS * kCBM;        // x loads per wave and tile
-  constexpr int kRow = kNS * kC * 2;     // bytes of one token's residual row
-  constexpr int kUnit = 2 * kNS;         // loads covering two column blocks of all streams
-  constexpr int kFragRows = kLd * kFragPerKB;
-  constexpr int kNW = kThreads / kWave;
-  constexpr int kUnits = kCBM / 2;       // column-block pairs per member and tile
-  // fused: the first raw load issued after a tile's record stores (step 1) is
-  // the next unit's, consumed at step kUnit
-  constexpr int kArrive = kFused ? kUnit : kPArrive;
-  static_assert(kC % (kKB * kPG) == 0 && kCBM % 2 == 0, "hidden size must split into column-block pairs");
-  static_assert(!(kFused && kGates), "the gates-only form has no post stage");
-  static_assert(kLd == 40 && kLd % kPQ == 0, "the exchange schedule assumes 40 loads per tile");
-  static_assert(kNW * kTileT == kPT, "one 16-token MFMA tile per wave");
-  __shared__ uint4 s_fnv[kLd * kFragPerKB * kWave];  // this member's weight: [stream*kCBM + block][frag][lane]
-  __shared__ uint4 s_w[kCBM][4];                    // this member's columns of the norm weight
-  __shared__ float s_red[kNW][kTileT][52];          // per wave: MFMA D layout -> token rows
-  __shared__ float4 s_xs[kNW][kPSsy / 4];             // per wave: loaded sum-y^2 block
-  __shared__ float4 s_xv[kNW][kPG * kPLine / 4];     // per wave: loaded value block of its gate token
-  __shared__ float s_gv[kNW][32];                   // per wave: the summed values of its gate token
-  __shared__ float s_ba[32];                        // bias[24], alpha[3]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int i = lane & 15;
-  const int g = lane >> 4;
-  const int mem = blockIdx.x % kPG;
-  const int grp = blockIdx.x / kPG;
-  const int ntiles = (p.T + kPT - 1) / kPT;
-  const int nk = (ntiles - 1 - grp) / ngroups + 1;   // tiles of this group (launch: ngroups <= ntiles)
-  const int cb0 = mem * kCBM;
-  const int xlane = (wave * kTileT + i) * kRow + g * 16;
-  const int plane = (wave * kTileT + i) * 16;
-  const int llane = (wave * kTileT + i) * (kC * 2) + g * 16;
-  const bool norm = p.nw != nullptr;
-
-  // descriptors of the group's k-th tile (k < 0 or k >= nk: zero bytes)
-  auto tile_of = [&](int k) { return (k >= 0 && k < nk) ? grp + k * ngroups : -1; };
-  auto tile_rows = [&](int t) { return t >= 0 ? min(kPT, p.T - t * kPT) : 0; };
-  auto x_rsrc = [&](int t) {
-    return make_rsrc(p.x + (size_t)max(t, 0) * kPT * (kNS * kC), tile_rows(t) * kRow);
-  };
-  auto pin_rsrc = [&](int t) { return make_rsrc(p.pre_in + (size_t)max(t, 0) * kPT * kNS, tile_rows(t) * 16); };
-  auto li_rsrc = [&](int t) { return make_rsrc(p.li + (size_t)max(t, 0) * kPT * kC, tile_rows(t) * kC * 2); };
-  // fused: sublayer output, next residual, the previous seam's post gates and comb
-  auto y_rsrc = [&](int t) { return make_rsrc(p.ysub + (size_t)max(t, 0) * kPT * kC, tile_rows(t) * kC * 2); };
-  auto xo_rsrc = [&](int t) {
-    return make_rsrc(p.xout + (size_t)max(t, 0) * kPT * (kNS * kC), tile_rows(t) * kRow);
-  };
-  auto gp_rsrc = [&](int t) { return make_rsrc(p.post_in + (size_t)max(t, 0) * kPT * kNS, tile_rows(t) * 16); };
-  auto gc_rsrc = [&](int t) { return make_rsrc(p.comb_in + (size_t)max(t, 0) * kPT * 16, tile_rows(t) * 64); };
-  const int xsoff = cb0 * kKB * 2;   // byte offset of this member's first column (SGPR)
-  int xls[kNS];                      // lane offset of each stream; the block offset fits the immediate
-#pragma unroll
-  for (int s = 0; s < kNS; ++s) xls[s] = xlane + s * kC * 2;
-  __asm__ volatile("" : "+v"(xls[0]), "+v"(xls[1]), "+v"(xls[2]), "+v"(xls[3]));
-  // load n of a tile: unit n / kUnit covers column blocks 2u, 2u + 1; within it
-  // stream-major, so loads 2q, 2q + 1 are the two halves of a 128-byte line
-  auto x_load = [&](rsrc_t r, int n) {
-    const int u = n / kUnit, q = n % kUnit;
-    const int s = q >> 1, cb = 2 * u + (q & 1);
-    return buf_load16(r, xls[s] + cb * kKB * 2, xsoff);
-  };
-  // fused: raw load `kind` of column block cb: 0 the sublayer output, 1 + s stream s
-  auto raw_load = [&](rsrc_t rxx, rsrc_t ryy, int kind, int cb) {
-    return kind == 0 ? buf_load16(ryy, llane + cb * kKB * 2, xsoff)
-                     : buf_load16(rxx, xls[kind - 1] + cb * kKB * 2, xsoff);
-  };
-
-  unsigned* cnt_base = p.cnt + kPCntBase + (grp * kNW + wave) * kPSlots * kPCntStride;
-  float* rec_base = p.part + (size_t)(grp * kNW + wave) * kPRing * kPRec;
-  // counter, arrival target and record of the group's k-th tile (k < 0: the scratch counter)
-  auto cnt_of = [&](int k) { return cnt_base + (k >= 0 ? k % kPRing : kPRing) * kPCntStride; };
-  // (p.wait_bias, zero in a normal call, puts every target out of reach)
-  auto target_of = [&](int k) {
-    return (k >= 0 ? (unsigned)kPG * (unsigned)(k / kPRing + 1) : 0u) + p.wait_bias;
-  };
-  auto rec_rsrc = [&](int k) {
-    return make_rsrc(rec_base + (size_t)(k >= 0 ? k % kPRing : 0) * kPRec, k >= 0 ? kPRec * 4 : 0);
-  };
-
-  // ---- prologue: the weight slice's loads first, then the first residual
-  // loads and pre_in, then the slice into LDS.  A wave's vector loads retire in
-  // issue order, so weight loads issued after the residual loads would each
-  // wait for those (HBM) as well.
-  constexpr int kFragPerWave = kFragRows / kNW;
-  static_assert(kFragRows % kNW == 0, "weight fragments split evenly over the waves");
-  uint4 fv[kFragPerWave];
-  {
-    const rsrc_t rf = make_rsrc(p.fnp, p.KB * kFragPerKB * kWave * 16);
-#pragma unroll
-    for (int u = 0; u < kFragPerWave; ++u) {
-      const int fr = wave + u * kNW;   // fragment row: (stream*kCBM + block)*3 + frag
-      const int lb = fr / kFragPerKB, f = fr - lb * kFragPerKB;
-      const int s = lb / kCBM, cb = lb - s * kCBM;
-      const int kbg = s * (kC / kKB) + cb0 + cb;
-      fv[u] = buf_load16(rf, ((kbg * kFragPerKB + f) * kWave + lane) * 16, 0);
-    }
-  }
-  rsrc_t rx = x_rsrc(tile_of(0));
-  rsrc_t ry = y_rsrc(tile_of(0));
-  uint4 xq[kPQ];
-  uint4 rq[5][2];   // fused: one unit's raw loads [sublayer output, streams 0..3][block of the pair]
-  uint4 gq[5];      // fused: the lane token's post gates, then its comb rows 0..3
-  if constexpr (kFused) {
-#pragma unroll
-    for (int kind = 0; kind < 5; ++kind)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) rq[kind][h] = raw_load(rx, ry, kind, h);
-    gq[0] = buf_load16(gp_rsrc(tile_of(0)), plane, 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) gq[1 + j] = buf_load16(gc_rsrc(tile_of(0)), plane * 4 + 16 * j, 0);
-  } else {
-#pragma unroll
-    for (int d = 0; d < kPQ; ++d) xq[d] = x_load(rx, d);
-  }
-  uint4 pq = make_uint4(0u, 0u, 0u, 0u);
-  if constexpr (!kGates) pq = buf_load16(pin_rsrc(tile_of(0)), plane, 0);
-#pragma unroll
-  for (int u = 0; u < kFragPerWave; ++u) s_fnv[(wave + u * kNW) * kWave + lane] = fv[u];
-  if (norm && tid < kCBM * 4) s_w[tid >> 2][tid & 3] = reinterpret_cast<const uint4*>(p.nw)[cb0 * 4 + tid];
-  if (tid < kNL) s_ba[tid] = p.bias[tid];
-  if (tid >= 32 && tid < 35) s_ba[kNL + tid - 32] = p.alpha[tid - 32];
-  __syncthreads();
-
-  float y0[kCBM][8];                // the current tile's collapsed rows (fused: parked as well)
-  float y1[kCBM][8], y2[kCBM][8];   // parked in AGPRs: the previous two tiles'
-  float yw[2][8];                   // fused: the current unit's two blocks while they accumulate
-  uint4 xp[kNS][2];                 // fused: the current unit's next-residual fragments
-#pragma unroll
-  for (int c = 0; c < kCBM; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y0[c][e] = kFused ? agpr_park(0.f) : 0.f;
-      y1[c][e] = y2[c][e] = agpr_park(0.f);
-    }
-  f32x4 pa0 = {0.f, 0.f, 0.f, 0.f}, pa1 = pa0, pa2 = pa0, pas = pa0;   // the last tile's accumulators
-  float pssy = 0.f;
-  uint4 pv[3];      // tile k-2's records, in flight: sum-y^2 block, gate token's values
-  unsigned cv = 0;  // tile k-2's arrival counter
-  TokenGates gt;
-  gt.m[0] = gt.m[1] = gt.m[2] = gt.m[3] = 1.0f;
-  gt.pr = gt.po = 0.0f;
-  gt.tok = -1;
-  gt.write = false;
-  gt.it = 0;
-
-  // weight fragments: two LDS base indices, each access within the 16-bit
-  // immediate offset of ds_read (the slice is 120 KB)
-  constexpr int kHalfLb = kLd / 2;
-  int fb0 = lane, fb1 = lane + kHalfLb * kFragPerKB * kWave;
-  __asm__ volatile("" : "+v"(fb0), "+v"(fb1));   // two bases: the compiler must not merge them
-  auto frag = [&](int lb, int f) -> uint4 {
-    return lb < kHalfLb ? s_fnv[fb0 + (lb * kFragPerKB + f) * kWave]
-                        : s_fnv[fb1 + ((lb - kHalfLb) * kFragPerKB + f) * kWave];
-  };
-  // the three weight fragments of load n's k-block, read one step ahead
-  uint4 fq[kFragPerKB];
-  auto fetch_frags = [&](int n) {
-    const int u = n / kUnit, q = n % kUnit;
-    const int lb = (q >> 1) * kCBM + 2 * u + (q & 1);
-#pragma unroll
-    for (int f = 0; f < kFragPerKB; ++f) fq[f] = frag(lb, f);
-  };
-  fetch_frags(0);
-
-  int budget = p.wait_budget;
-  auto wait_count = [&](const unsigned* c, unsigned target, unsigned v) {
-    while ((int)(v - target) < 0 && budget > 0) {
-      --budget;
-      __builtin_amdgcn_s_sleep(2);
-      v = ld_agent(c);
-    }
-    if ((int)(v - target) < 0 && lane == 0)
-      __hip_atomic_store(p.cnt + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // every load of this wave is complete when the loop ends, so the straight
-    // path's wait counts stay valid after it
-    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-  };
-  // the group's records of tile kk: the 1 KB sum-y^2 block and the 2 KB of
-  // the gate token (member index), whole lines
-  auto load_records = [&](int kk) {
-    const rsrc_t rr = rec_rsrc(kk);
-    pv[0] = buf_load16_agent(rr, lane * 16, 0);
-    pv[1] = buf_load16_agent(rr, (kPSsy + mem * kPG * kPLine) * 4 + lane * 16, 0);
-    pv[2] = buf_load16_agent(rr, (kPSsy + mem * kPG * kPLine) * 4 + (kWave + lane) * 16, 0);
-  };
-  // the loaded records into this wave's LDS staging
-  auto stage_records = [&]() {
-    s_xs[wave][lane] = __builtin_bit_cast(float4, pv[0]);
-    s_xv[wave][lane] = __builtin_bit_cast(float4, pv[1]);
-    s_xv[wave][kWave + lane] = __builtin_bit_cast(float4, pv[2]);
-  };
-  // norm factor of token i
-  auto sum_ssy = [&]() {
-    const float* xs = reinterpret_cast<const float*>(s_xs[wave]);
-    // token i, members 4g..4g+3, then the four groups: the same order in every member
-    const float sg = ((xs[(4 * g) * kTileT + i] + xs[(4 * g + 1) * kTileT + i]) + xs[(4 * g + 2) * kTileT + i]) +
-                     xs[(4 * g + 3) * kTileT + i];
-    float sy = sg + __shfl_xor(sg, 16);
-    sy = sy + __shfl_xor(sy, 32);
-    return norm ? 1.0f / sqrtf(sy / (float)kC + p.eps) : 1.0f;
-  };
-  // the gate token's summed values (-> s_gv), members in order
-  auto sum_gate = [&]() {
-    const float* xv = reinterpret_cast<const float*>(s_xv[wave]);
-    if (lane < kPVals) {
-      float acc = 0.f;
-#pragma unroll
-      for (int m = 0; m < kPG; ++m) acc += xv[m * kPLine + lane];
-      s_gv[wave][lane] = acc;
-    }
-  };
-  // one 32-column block of layer_input; parked (AGPR) or live values
-  auto li_store = [&](const float (&yin)[8], bool parked, float ry, rsrc_t rl, int cb) {
-    float yb[8], o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) yb[e] = parked ? agpr_read(yin[e]) : yin[e];
-    if (norm) {
-      float w[8];
-      unpack8(s_w[cb][g], w);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (yb[e] * ry) * w[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = yb[e];
-    }
-    buf_store16(pack8(o), rl, llane + cb * kKB * 2, xsoff);
-  };
-
-  // the last tile's partial sums: accumulators (MFMA D layout) -> token rows in LDS
-  auto publish_a = [&]() {
-    float ssx = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (i == 4 * g + r) ssx = pas[r];
-    float t = pssy + __shfl_xor(pssy, 16);
-    t += __shfl_xor(t, 32);
-    float (*red)[52] = s_red[wave];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      red[4 * g + r][i] = pa0[r];
-      red[4 * g + r][16 + i] = pa1[r];
-      red[4 * g + r][32 + i] = pa2[r];
-    }
-    if ((i >> 2) == g) red[i][48] = ssx;
-    if (g == 0) red[i][49] = t;
-  };
-  // ... and -> record of the group's kk-th tile, whole lines, no wait
-  auto publish_b = [&](int kk) {
-    const float (*red)[52] = s_red[wave];
-    const rsrc_t rr = rec_rsrc(kk);
-    // value block: this member's line of each token, 128 chunks of 16 B (chunk
-    // c: token c >> 3, values 4 (c & 7) .. +3; P = hi + lo, then sum x^2, zeros)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = h * kWave + lane;
-      const int tt = c >> 3, v0 = 4 * (c & 7);
-      float o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = v0 + e;
-        o[e] = j < kNL ? red[tt][j] + red[tt][kNL + j] : j == kNL ? red[tt][48] : 0.f;
-      }
-      buf_store16_agent(make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
-                                   __float_as_uint(o[3])),
-                        rr, (kPSsy + (tt * kPG + mem) * kPLine + v0) * 4, 0);
-    }
-    // sum-y^2 block: this member's 16 tokens, 64 bytes
-    if (lane < 4)
-      buf_store16_agent(make_uint4(__float_as_uint(red[4 * lane][49]), __float_as_uint(red[4 * lane + 1][49]),
-                                   __float_as_uint(red[4 * lane + 2][49]), __float_as_uint(red[4 * lane + 3][49])),
-                        rr, (mem * kTileT + 4 * lane) * 4, 0);
-  };
-
-  // One tile: sweep of the group's k-th tile into ycur; exchange of tiles k-1
-  // and k-2, and tile k-2's layer_input from yold.
-  auto tile_body = [&](int k, float (&ycur)[kCBM][8], float (&y1)[kCBM][8], float (&y2)[kCBM][8])
-                       __attribute__((always_inline)) {
-#pragma clang fp contract(off)
-    // re-define the base offsets in every tile, so that base + constant is
-    // formed here (and folds into the instructions' offset fields) instead of
-    // being hoisted into one register per access
-    __asm__ volatile("" : "+v"(xls[0]), "+v"(xls[1]), "+v"(xls[2]), "+v"(xls[3]), "+v"(fb0), "+v"(fb1));
-    const int tnext = tile_of(k + 1);
-    const rsrc_t rxn = x_rsrc(tnext);
-    const rsrc_t ryn = y_rsrc(tnext);
-    const rsrc_t rxo = xo_rsrc(tile_of(k));
-    const float p0 = __uint_as_float(pq.x), p1 = __uint_as_float(pq.y);
-    const float p2 = __uint_as_float(pq.z), p3 = __uint_as_float(pq.w);
-    unsigned* cnt1 = cnt_of(k - 1);
-    const int t2 = tile_of(k - 2);
-    const rsrc_t rl2 = li_rsrc(t2);
-    unsigned* cnt2 = cnt_of(k - 2);
-    const unsigned target2 = target_of(k - 2);
-    float ry2 = 1.0f;
-
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, as = a0;
-    float ssy = 0.f;
-#pragma unroll
-    for (int n = 0; n < kLd; ++n) {
-      // Sinkhorn of the previous gate token: a chain of dependent arithmetic,
-      // first in the step so that it overlaps the wait for this step's x
-      if (n < kPGateEnd || n >= kPIter) gt.step(p.iters);
-      if (n == kPGateEnd) gt.finish(p);
-      const int u = n / kUnit, q = n % kUnit;
-      const int s = q >> 1, cb = 2 * u + (q & 1);
-      if constexpr (kFused) {
-        if (q < 2) {
-          // the post stage for block cb: its four next-residual fragments, written out
-          float yf[8], a0[8], a1[8], a2[8], a3[8];
-          unpack8(rq[0][q], yf);
-          unpack8(rq[1][q], a0);
-          unpack8(rq[2][q], a1);
-          unpack8(rq[3][q], a2);
-          unpack8(rq[4][q], a3);
-#pragma unroll
-          for (int t = 0; t < kNS; ++t) {
-            xp[t][q] = post_stream8(u4_comp(gq[0], t), u4_comp(gq[1 + t], 0), u4_comp(gq[1 + t], 1),
-                                    u4_comp(gq[1 + t], 2), u4_comp(gq[1 + t], 3), yf, a0, a1, a2, a3);
-            buf_store16(xp[t][q], rxo, xls[t] + cb * kKB * 2, xsoff);
-          }
-        }
-      }
-      const uint4 xv = kFused ? xp[s][q & 1] : xq[n % kPQ];
-      a0 = mfma_bf16(xv, fq[0], a0);
-      a1 = mfma_bf16(xv, fq[1], a1);
-      a2 = mfma_bf16(xv, fq[2], a2);
-      as = mfma_bf16(xv, xv, as);
-      // the next step's weight fragments (the order of k-blocks is the same in every tile)
-      fetch_frags((n + 1) % kLd);
-      float f[8];
-      unpack8(xv, f);
-      const float ps = s == 0 ? p0 : s == 1 ? p1 : s == 2 ? p2 : p3;
-      if constexpr (kFused) {
-        // all three row buffers are parked; the unit's two blocks accumulate in
-        // registers and are parked once complete
-        const int h = q & 1;
-        if (s == 0) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            y2[cb][e] = agpr_move(y1[cb][e]);
-            y1[cb][e] = agpr_move(y0[cb][e]);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) yw[h][e] = s == 0 ? ps * f[e] : yw[h][e] + ps * f[e];
-        if (s == kNS - 1) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(yw[h][e], yw[h][e], ssy);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y0[cb][e] = agpr_park(yw[h][e]);
-        }
-      } else if (!kGates && s == 0) {
-        // the buffers move down one place, block by block, just before this
-        // tile's first write of the block: tile k-1's rows are parked, tile
-        // k-2's rows move to the oldest buffer
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          y2[cb][e] = agpr_move(y1[cb][e]);
-          y1[cb][e] = agpr_park(ycur[cb][e]);
-        }
-      }
-      if constexpr (!kFused) {
-        if constexpr (!kGates) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ycur[cb][e] = s == 0 ? ps * f[e] : ycur[cb][e] + ps * f[e];
-          if (s == kNS - 1) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ssy = __builtin_fmaf(ycur[cb][e], ycur[cb][e], ssy);
-          }
-        }
-        // refill: this tile's load n + kPQ, or the next tile's first loads
-        const int m = n + kPQ;
-        if (m < kLd) {
-          xq[n % kPQ] = x_load(rx, m);
-        } else {
-          xq[n % kPQ] = x_load(rxn, m - kLd);
-          if (!kGates && m == kLd) pq = buf_load16(pin_rsrc(tnext), plane, 0);
-        }
-      }
-      // ---- exchange of tile k-1
-      if (n == kPPubA) publish_a();
-      if (n == kPPubB) publish_b(k - 1);
-      if (n == kArrive) {
-        // the first x load issued after tile k-1's records were stored has returned
-        const unsigned z = zero_after(kFused ? rq[0][0].x : xv.x);
-        if (lane == 0) __hip_atomic_fetch_add(cnt1, 1u + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      // ---- exchange of tile k-2 and its layer_input
-      if (n == kPCnt) {
-        cv = ld_agent(cnt2);
-        __asm__ volatile("" ::: "memory");   // keep the read here, kPCheck - kPCnt steps ahead of its use
-      }
-      if (n == kPCheck) {
-        cv += zero_after(xv.y);              // the check cannot move above this step
-        if ((int)(cv - target2) < 0) wait_count(cnt2, target2, cv);
-        load_records(k - 2);
-        __asm__ volatile("" ::: "memory");   // issued here, used kPStage - kPCheck steps later
-      }
-      if (n == kPStage) stage_records();
-      if (n == kPSumY) ry2 = sum_ssy();
-      if (n == kPSumG) sum_gate();
-      if (n == kPInit) gt.init_a(p, s_gv[wave], s_ba, t2 * kPT + wave * kTileT + mem, t2 >= 0);
-      if (n == kPInit + 1) gt.init_b();
-      if (n == kPInit + 2) gt.init_c();
-      // layer_input of tile k-2, one block per step, each after its block moved
-      // to the oldest buffer (blocks 8 and 9 move at steps 32 and 33)
-      {
-        constexpr int kLiStep[kCBM] = {22, 23, 24, 25, 26, 27, 28, 29, 34, 35};
-#pragma unroll
-        for (int c = 0; c < kCBM; ++c)
-          if (!kGates && n == kLiStep[c]) li_store(y2[c], true, ry2, rl2, c);
-      }
-      // fused refill, once the unit's raw loads are consumed (and after this
-      // step's record stores): the next unit, or the next tile's first unit
-      // with its pre_in and gates
-      if constexpr (kFused) {
-        if (q == 1) {
-          __asm__ volatile("" ::: "memory");
-          if (u + 1 < kUnits) {
-#pragma unroll
-            for (int kind = 0; kind < 5; ++kind)
-#pragma unroll
-              for (int h = 0; h < 2; ++h) rq[kind][h] = raw_load(rx, ry, kind, 2 * (u + 1) + h);
-          } else {
-#pragma unroll
-            for (int kind = 0; kind < 5; ++kind)
-#pragma unroll
-              for (int h = 0; h < 2; ++h) rq[kind][h] = raw_load(rxn, ryn, kind, h);
-            pq = buf_load16(pin_rsrc(tnext), plane, 0);
-            gq[0] = buf_load16(gp_rsrc(tnext), plane, 0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) gq[1 + j] = buf_load16(gc_rsrc(tnext), plane * 4 + 16 * j, 0);
-          }
-        }
-      }
-    }
-    rx = rxn;
-    ry = ryn;
-
-    pa0 = a0;
-    pa1 = a1;
-    pa2 = a2;
-    pas = as;
-    pssy = ssy;
-  };
-
-  // After the last tile kl: its partial sums, then the exchange and
-  // layer_input of tiles kl-1 (buffer y2) and kl (buffer y1), waiting as
-  // needed.
-  auto finish_tile = [&](int kk, const float (&yb)[kCBM][8], bool parked) __attribute__((always_inline)) {
-    unsigned* c = cnt_of(kk);
-    const unsigned v = ld_agent(c);
-    if ((int)(v - target_of(kk)) < 0) wait_count(c, target_of(kk), v);
-    load_records(kk);
-    stage_records();
-    const float ry = sum_ssy();
-    sum_gate();
-    const int t = tile_of(kk);
-    gt.init(p, s_gv[wave], s_ba, t * kPT + wave * kTileT + mem, t >= 0);
-    const rsrc_t rl = li_rsrc(t);
-#pragma unroll
-    for (int cb = 0; cb < kCBM; ++cb)
-      if (!kGates) li_store(yb[cb], parked, ry, rl, cb);
-    gt.finish(p);
-  };
-
-  // one instance of the tile body (its code must stay small enough for the
-  // instruction cache); tile k fills y0 while y1, y2 hold tiles k-1, k-2
-  for (int k = 0; k < nk; ++k) tile_body(k, y0, y1, y2);
-  const int kl = nk - 1;
-  gt.finish(p);
-  publish_a();
-  publish_b(kl);
-  wait_vmem();   // tile kl's records are stored
-  if (lane == 0) __hip_atomic_fetch_add(cnt_of(kl), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (kl >= 1) finish_tile(kl - 1, y1, true);
-  finish_tile(kl, y0, kFused);
-
-  // ---- the last wave of the grid to finish resets the counters
-  wait_vmem();
-  unsigned old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(p.cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0);
-  if (old == gridDim.x * kNW - 1) {
-    const int ncnt = ngroups * kNW * kPSlots;
-    for (int c = lane; c < ncnt; c += kWave)
-      __hip_atomic_store(p.cnt + kPCntBase + c * kPCntStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane == 0) __hip_atomic_store(p.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
+// ------------------------------------------------------------------ pre kernel, persistent form
+}  // namespace mhc
+#include "mhc_persist.hpp"
+namespace mhc {
 
 // ------------------------------------------------------------------ standalone collapse
 // One workgroup per token: the exact-order collapse with p[token] and the

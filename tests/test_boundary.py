@@ -69,7 +69,11 @@ def test_sizes():
     assert m.mhc_workspace_bytes(3073, 4, C) == m.mhc_workspace_bytes(16384, 4, C)
     assert m.mhc_workspace_bytes(16384, 4, C) < 16 * MiB
     assert m.mhc_workspace_bytes(1 << 20, 4, C) == m.mhc_workspace_bytes(16384, 4, C)
-    assert m.mhc_workspace_bytes(1 << 20, 4, 4096) < 2 * MiB   # no grouped form for C != 5120
+    # hidden sizes with a persistent form (4096, 5120, 7168) need its records; others do not
+    assert m.mhc_workspace_bytes(1 << 20, 4, 4096) == m.mhc_workspace_bytes(16384, 4, 4096) < 16 * MiB
+    assert m.mhc_workspace_bytes(1 << 20, 4, 7168) == m.mhc_workspace_bytes(16384, 4, 7168) < 16 * MiB
+    assert m.mhc_workspace_bytes(1 << 20, 4, 1024) < 2 * MiB
+    assert m.mhc_workspace_bytes(1 << 20, 4, 6144) < 2 * MiB
     assert m.mhc_workspace_bytes(16, 3, C) == 0
     assert m.mhc_workspace_bytes(16, 4, 5000) == 0
     for s in range(8):
@@ -212,7 +216,8 @@ def test_workspace_needs_by_form():
     assert call_pre(T=4096, ws=None) == HIP
     assert call_pre(T=4097, ws=None) == WS
     assert call_pre(T=4097, ws_bytes=m.mhc_workspace_bytes(4097, 4, C)) == HIP
-    assert call_pre(T=6001, C=4096, ws=None) == HIP
+    assert call_pre(T=6001, C=4096, ws=None) == WS             # persistent gates-only form at C = 4096 too
+    assert call_pre(T=6001, C=6144, ws=None) == HIP            # no persistent form: one workgroup per tile
 
 
 class FarPtrs(Ptrs):
