@@ -8,7 +8,7 @@ built, importing the ops raises.
 
 Entry points (same names as the C ABI):
     mhc_pack_fn, mhc_pre, mhc_pre_delayed, mhc_post, mhc_post_pre_delayed,
-    mhc_broadcast_entry, mhc_collapse, mhc_workspace_bytes, mhc_fn_packed_bytes,
+    mhc_post_pre_delayed_noalloc, mhc_broadcast_entry, mhc_collapse, mhc_workspace_bytes, mhc_fn_packed_bytes,
     mhc_status_str, mhc_debug_force_wait_timeouts (test hook)
 """
 from __future__ import annotations
@@ -62,8 +62,10 @@ def lib() -> ctypes.CDLL:
         L.mhc_broadcast_entry.argtypes = [P, I, I, I, _Weights, P, F, I, P, P, P, P, P, P, Z, P]
         L.mhc_collapse.argtypes = [P, P, I, I, I, P, F, P, P]
         L.mhc_post_pre_delayed.argtypes = [P, P, P, P, P, I, I, I, _Weights, P, F, I, P, P, P, P, P, P, Z, P]
+        L.mhc_post_pre_delayed_noalloc.argtypes = [P, P, P, P, P, I, I, I, _Weights, P, F, I, P, P, P, P,
+                                                   P, P]
         for f in ("mhc_pack_fn", "mhc_pre", "mhc_pre_delayed", "mhc_post", "mhc_post_pre_delayed",
-                  "mhc_broadcast_entry",
+                  "mhc_post_pre_delayed_noalloc", "mhc_broadcast_entry",
                   "mhc_collapse"):
             getattr(L, f).restype = I
         L.mhc_debug_force_wait_timeouts.argtypes = [I]
@@ -75,7 +77,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("mhc_fn_packed_bytes", "mhc_pack_fn", "mhc_workspace_bytes", "mhc_pre",
-           "mhc_pre_delayed", "mhc_post", "mhc_post_pre_delayed", "mhc_broadcast_entry", "mhc_collapse",
+           "mhc_pre_delayed", "mhc_post", "mhc_post_pre_delayed", "mhc_post_pre_delayed_noalloc",
+           "mhc_broadcast_entry", "mhc_collapse",
            "mhc_status_str", "mhc_debug_force_wait_timeouts")
 
 # Workspace byte offsets (include/mhc.h): the region calls leave zero, and the
@@ -85,6 +88,7 @@ WS_WAIT_ERROR_PERSIST = 8
 WS_WAIT_ERROR_SPLIT = 96 * 1024 + 1024
 MAX_TOKENS = 1 << 22
 MAX_SINKHORN_ITERS = 1024
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 def mhc_debug_force_wait_timeouts(sleeps: int) -> None:
@@ -383,6 +387,35 @@ def mhc_post_pre_delayed(y, x, post_in, comb_in, pre_in, w: Weights, norm_weight
                                     _ptr(_u16(x_out)), _ptr(pre), _ptr(post), _ptr(comb), _ptr(li),
                                     _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "mhc_post_pre_delayed")
+    return x_out, pre, post, comb, li
+
+
+def mhc_post_pre_delayed_noalloc(y, x, post_in, comb_in, pre_in, w: Weights, norm_weight=None, eps=1e-6,
+                                 iters=20, out=None):
+    """mhc_post_pre_delayed with the library's own per-GPU scratch buffer instead of a workspace:
+    the C call allocates nothing (pass `out` = (x_out, pre_out, post, comb, layer_input) to keep
+    this wrapper from allocating them).  Calls that overlap on one GPU race."""
+    torch = _torch()
+    T, n, C, dev = _residual(x)
+    _arg(y, "y", (T, C), "bf16", dev)
+    _arg(post_in, "post_in", (T, n), "f32", dev)
+    _arg(comb_in, "comb_in", (T, n, n), "f32", dev)
+    _arg(pre_in, "pre_in", (T, n), "f32", dev)
+    _weights_arg(w, n * C, dev)
+    _arg(norm_weight, "norm_weight", (C,), "bf16", dev, optional=True)
+    _scalars(eps, iters)
+    if out is None:
+        x_out = torch.empty_like(x)
+        pre, post, comb, li = _pre_outputs(T, C, dev)
+    else:
+        x_out, pre, post, comb, li = out
+    _arg(x_out, "x_out", (T, n, C), "bf16", dev)
+    _check_pre_outs((pre, post, comb, li), T, C, dev)
+    st = lib().mhc_post_pre_delayed_noalloc(_ptr(_u16(y)), _ptr(_u16(x)), _ptr(post_in), _ptr(comb_in),
+                                            _ptr(pre_in), T, n, C, w.as_c(), _ptr(_u16(norm_weight)),
+                                            float(eps), int(iters), _ptr(_u16(x_out)), _ptr(pre), _ptr(post),
+                                            _ptr(comb), _ptr(li), _stream(dev))
+    _check(st, "mhc_post_pre_delayed_noalloc")
     return x_out, pre, post, comb, li
 
 

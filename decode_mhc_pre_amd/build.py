@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmhc.so")
 SOURCES = [os.path.join(CSRC, "mhc.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("mhc_device.hpp", "mhc_kernels.hpp")] + \
+DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("mhc_device.hpp", "mhc_kernels.hpp", "mhc_persist.hpp")] + \
     [os.path.join(INCLUDE, "mhc.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "mhc.h"
 #include "mhc_kernels.hpp"
@@ -215,6 +216,61 @@ void launch_persist(int mode, const PreParams& p, int ng, hipStream_t s) {
     hipLaunchKernelGGL((mhc_persist_kernel<kC, false, true>), grid, block, 0, s, p, ng);
 }
 
+// ------------------------------------------------------------------ no-allocation variant
+// A workspace in device memory the library owns: one per GPU (each device
+// holds its own copy of the array), used by mhc_post_pre_delayed_noalloc for
+// callers that cannot allocate.  Its size covers every plan of the fused seam
+// (the persistent kernels' records at the largest group, the split form's
+// partial sums at the most tiles x splits a plan has).
+constexpr size_t kScratchBytes = MHC_NOALLOC_SCRATCH_BYTES;
+static_assert(kPPartOffset + (size_t)kPMaxGroups * kPW * kPRing * persist_rec_floats(kPMaxPG) * sizeof(float) <=
+                  kScratchBytes,
+              "scratch too small for the persistent records");
+static_assert(kPPartOffset + (size_t)kMaxSplitTiles * 2 * kTileT * kPartStride * sizeof(float) <= kScratchBytes,
+              "scratch too small for the split partial sums");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` per device (the array's name is a host-side
+// stand-in, not a device address), taken once with that device current, and
+// whether its flag region has been cleared since (not under graph capture: a
+// captured clear runs only on replay).
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+bool g_scratch_clear[64];
+
+__global__ __launch_bounds__(256) void mhc_clear_kernel(uint4* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+mhc_status scratch_of(hipStream_t s, void** out) {
+  hipDevice_t dev = 0;
+  if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= 64) return MHC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return MHC_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return MHC_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return MHC_ERR_HIP;
+    if (e != hipSuccess || ptr == nullptr) return MHC_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  if (!g_scratch_clear[dev]) {
+    // the words calls read before they write start at zero (every call leaves them so)
+    const int n = (int)(kPPartOffset / 16);
+    hipLaunchKernelGGL(mhc_clear_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
+                       static_cast<uint4*>(g_scratch_ptr[dev]), n);
+    if (hipGetLastError() != hipSuccess) return MHC_ERR_HIP;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return MHC_ERR_HIP;
+    if (cs == hipStreamCaptureStatusNone) g_scratch_clear[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
+  return MHC_OK;
+}
+
 // The previous seam's post-stage inputs of the fused form.
 struct PostIn {
   const uint16_t* y;
@@ -226,7 +282,8 @@ struct PostIn {
 mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, int n, int C,
                       mhc_weights w, const uint16_t* norm_weight, float eps, int iters,
                       uint16_t* x_out, float* pre, float* post, float* comb, uint16_t* li,
-                      void* ws, size_t ws_bytes, void* stream, PostIn pi = {nullptr, nullptr, nullptr}) {
+                      void* ws, size_t ws_bytes, void* stream, PostIn pi = {nullptr, nullptr, nullptr},
+                      bool noalloc = false) {
   mhc_status st = check_common(T, n, C);
   if (st != MHC_OK) return st;
   if ((st = check_scalars(eps, iters)) != MHC_OK) return st;
@@ -264,6 +321,11 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   if (any_alias(outs, 6, ins, 9)) return MHC_ERR_ALIAS;
 
   if (T == 0) return MHC_OK;
+  if (noalloc) {
+    // the library's own buffer instead of a workspace, once the arguments are known good
+    if ((st = scratch_of(static_cast<hipStream_t>(stream), &ws)) != MHC_OK) return st;
+    ws_bytes = kScratchBytes;
+  }
   Plan pl = make_plan(T, KB, mode, entry ? 0 : persist_pg(C));
   const size_t need = plan_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return MHC_ERR_WORKSPACE;
@@ -304,8 +366,8 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
   // for its tile's pre-mix (instead of the tile's last arriver collapsing all
   // of its tokens after the gates)
   p.own_wgs = (!delayed && pl.nsplit > 1 && C <= kWaveCollapseMaxC && T <= kOwnMaxTokens) ? 1 : 0;
-  p.wait_bias = g_wait_bias;
-  p.wait_budget = g_wait_budget;
+  p.wait_bias = noalloc ? 0u : g_wait_bias;
+  p.wait_budget = noalloc ? kWaitBudget : g_wait_budget;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 block(kThreads);
@@ -450,6 +512,16 @@ mhc_status mhc_post_pre_delayed(const uint16_t* y, const uint16_t* x, const floa
   return pre_common(kModeFused, x, pre_in, T, n, C, w, norm_weight, eps, sinkhorn_iters, x_out,
                     pre_out, post, comb, layer_input, workspace, workspace_bytes, stream,
                     PostIn{y, post_in, comb_in});
+}
+
+mhc_status mhc_post_pre_delayed_noalloc(const uint16_t* y, const uint16_t* x, const float* post_in,
+                                        const float* comb_in, const float* pre_in, int T, int n, int C,
+                                        mhc_weights w, const uint16_t* norm_weight, float eps,
+                                        int sinkhorn_iters, uint16_t* x_out, float* pre_out, float* post,
+                                        float* comb, uint16_t* layer_input, void* stream) {
+  return pre_common(kModeFused, x, pre_in, T, n, C, w, norm_weight, eps, sinkhorn_iters, x_out, pre_out,
+                    post, comb, layer_input, nullptr, 0, stream, PostIn{y, post_in, comb_in},
+                    /*noalloc=*/true);
 }
 
 mhc_status mhc_post(const uint16_t* y, const uint16_t* x, const float* post, const float* comb,

@@ -90,8 +90,9 @@ mhc_status mhc_pack_fn(const float *fn, int K, void *fn_packed, void *stream);
 /* Workspace bytes needed by mhc_pre, mhc_pre_delayed, mhc_post_pre_delayed and
  * mhc_broadcast_entry for any T <= T_max with this n and C (few tokens: the
  * projection is split over workgroups that combine partial sums in it; with
- * C = 5120 the persistent kernels of mhc_post_pre_delayed (T > 3072),
- * mhc_pre_delayed and mhc_pre (T > 4096) exchange partial sums through it).  One
+ * C = 4096, 5120 or 7168 the persistent kernels of mhc_post_pre_delayed
+ * (T > 3072), mhc_pre_delayed and mhc_pre (T > 4096) exchange partial sums
+ * through it: about 4.5 MB at C = 5120 and 7.8 MB at C = 7168).  One
  * workspace serves all of these calls.  The caller zero-fills it once after
  * allocating it; every call leaves its counters back
  * at zero, so it can be reused (and captured) without clearing. */
@@ -190,8 +191,8 @@ mhc_status mhc_post(const uint16_t *y, const uint16_t *x, const float *post,
  *            rounded once (the same bits as mhc_post).
  *   pre_out, post, comb, layer_input: seam k+1's outputs, from x_out, as in
  *            mhc_pre_delayed.
- * Launches: one; at hidden sizes other than 5120 and T > 3072, the post kernel
- * and then the delayed pre kernel.  The
+ * Launches: one; at hidden sizes other than 4096, 5120 and 7168 and T > 3072,
+ * the post kernel and then the delayed pre kernel.  The
  * workspace is that of mhc_pre_delayed (mhc_workspace_bytes).  x_out must not
  * overlap x or any other argument: this form is not in place (MHC_ERR_ALIAS). */
 mhc_status mhc_post_pre_delayed(const uint16_t *y, const uint16_t *x,
@@ -202,6 +203,31 @@ mhc_status mhc_post_pre_delayed(const uint16_t *y, const uint16_t *x,
                                 float *pre_out, float *post, float *comb,
                                 uint16_t *layer_input, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/* mhc_post_pre_delayed for callers that cannot allocate device memory or
+ * bring a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments and results are those of
+ * mhc_post_pre_delayed (same kernels, same bits) without the workspace pair:
+ * the exchange workspace is a buffer of MHC_NOALLOC_SCRATCH_BYTES in device
+ * memory that the library holds on each GPU it runs on until the process
+ * ends.  The call allocates nothing; the first call on a device looks up that
+ * device's buffer and enqueues a clear of its flag region on `stream`.
+ * Every shape mhc_post_pre_delayed accepts fits the buffer (the largest need
+ * is the persistent kernels' at C = 7168, about 7.8 MB); a call whose plan
+ * would need more returns MHC_ERR_WORKSPACE.  All calls on one GPU share the
+ * buffer: calls that overlap on a device (other streams, other host threads
+ * without ordering between them) race and give unspecified results.  The
+ * waits of this form are bounded as described above; a run-out here is not
+ * reported (the wait-error words live in the shared buffer) and
+ * mhc_debug_force_wait_timeouts does not apply to it. */
+#define MHC_NOALLOC_SCRATCH_BYTES (8u << 20)
+mhc_status mhc_post_pre_delayed_noalloc(const uint16_t *y, const uint16_t *x,
+                                        const float *post_in, const float *comb_in,
+                                        const float *pre_in, int T, int n, int C,
+                                        mhc_weights w, const uint16_t *norm_weight,
+                                        float eps, int sinkhorn_iters, uint16_t *x_out,
+                                        float *pre_out, float *post, float *comb,
+                                        uint16_t *layer_input, void *stream);
 
 /* Model-entry seam (p1 Summary and Approach: the broadcast seam projects a
  * narrower operand).  The single stream h[T][C] bf16 is broadcast to all n

@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol():
 
 
 RUNTIME_ALLOWED = {"hipLaunchKernel", "hipGetLastError", "hipStreamGetDevice", "hipDeviceGetAttribute",
-                   "__hipPushCallConfiguration", "__hipPopCallConfiguration", "__hipRegisterFatBinary",
+                   "hipStreamIsCapturing", "hipGetSymbolAddress", "hipGetDevice", "hipSetDevice",
+                   "__hipPushCallConfiguration", "__hipRegisterVar", "__hipPopCallConfiguration", "__hipRegisterFatBinary",
                    "__hipRegisterFunction", "__hipUnregisterFatBinary"}
 
 
@@ -52,9 +53,11 @@ def test_library_imports_no_allocating_or_blocking_runtime_call():
     used = {ln.split()[-1].split("@")[0] for ln in out.splitlines() if ln.strip()}
     hip = {s for s in used if s.startswith(("hip", "__hip")) or "hiprtc" in s}
     assert hip and hip <= RUNTIME_ALLOWED, sorted(hip - RUNTIME_ALLOWED)
-    # the persistent kernels' grid is sized from the launch stream's device, never
-    # from the calling thread's current device (which may be another GPU)
-    assert "hipStreamGetDevice" in hip and "hipGetDevice" not in hip
+    # the persistent kernels' grid and the no-allocation buffer follow the launch
+    # stream's device, not the calling thread's current device (which may be
+    # another GPU); the current device is only switched to look the buffer up
+    # and then restored
+    assert "hipStreamGetDevice" in hip and "hipGetSymbolAddress" in hip
 
 
 def test_sizes():
@@ -342,3 +345,46 @@ def test_workspace_offsets_match_header():
     assert max(m.WS_WAIT_ERROR_PERSIST, m.WS_WAIT_ERROR_SPLIT) + 4 <= m.WS_FLAG_BYTES
     # every plan's workspace holds the whole flag region
     assert m.mhc_workspace_bytes(8) >= m.WS_FLAG_BYTES
+
+
+def call_noalloc(**kw):
+    a = _pre_args(**kw)
+    P = Ptrs()
+    P.next = 0x80000000000
+    for k in ("y", "post_in", "comb_in", "xo"):
+        a.setdefault(k, kw.get(k, P()))
+    return m.lib().mhc_post_pre_delayed_noalloc(a["y"], a["x"], a["post_in"], a["comb_in"], a["pre_in"], a["T"],
+                                                a["n"], a["C"], a["w"], a["nw"], a["eps"], a["iters"], a["xo"],
+                                                a["pre"], a["post"], a["comb"], a["li"], None)
+
+
+def test_noalloc_validation():
+    """The no-allocation seam rejects what mhc_post_pre_delayed rejects, before it looks up its
+    buffer (no GPU here: a call that passes every check then fails in the runtime)."""
+    assert call_noalloc(n=3) == UNSUP
+    assert call_noalloc(C=5000) == UNSUP
+    assert call_noalloc(T=-1) == SHAPE
+    assert call_noalloc(T=(1 << 22) + 1) == SHAPE
+    assert call_noalloc(iters=0) == SHAPE
+    assert call_noalloc(iters=1025) == SHAPE
+    assert call_noalloc(eps=float("nan")) == SHAPE
+    for k in ("y", "x", "post_in", "comb_in", "xo", "pre_in", "pre", "post", "comb", "li"):
+        assert call_noalloc(**{k: None}) == NULL, k
+    assert call_noalloc(post_in=0x80000000004) == ALIGN
+    P = Ptrs()
+    x = P()
+    assert call_noalloc(x=x, xo=x) == ALIAS
+    g = P()
+    assert call_noalloc(pre_in=g, pre=g) == ALIAS
+    assert call_noalloc(T=0) == OK
+    assert call_noalloc() == HIP
+
+
+def test_noalloc_scratch_covers_every_plan():
+    """The library's own buffer holds the workspace of every shape the seam accepts."""
+    hdr = open(os.path.join(ROOT, "include", "mhc.h")).read()
+    mm = re.search(r"#define MHC_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert mm and int(mm.group(1)) << int(mm.group(2)) == m.NOALLOC_SCRATCH_BYTES
+    for c in range(256, 16384 + 1, 256):
+        for t in (1, 16, 33, 512, 2048, 3072, 3073, 4096, 4097, 1 << 22):
+            assert m.mhc_workspace_bytes(t, 4, c) <= m.NOALLOC_SCRATCH_BYTES, (t, c)
