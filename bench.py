@@ -66,8 +66,8 @@ def entry_bytes(T, C=C, norm=True):
     return T * (C * 2 + NS * C * 2 + C * 2 + 96) + C * 24 * 4 + 108 + (C * 2 if norm else 0)
 
 
-KERNEL_SOURCES = ("decode_mhc_pre_amd/csrc/mhc_kernels.hpp", "decode_mhc_pre_amd/csrc/mhc_device.hpp",
-                  "decode_mhc_pre_amd/csrc/mhc.hip")
+KERNEL_SOURCES = ("decode_mhc_pre_amd/csrc/mhc_kernels.hpp", "decode_mhc_pre_amd/csrc/mhc_persist.hpp",
+                  "decode_mhc_pre_amd/csrc/mhc_device.hpp", "decode_mhc_pre_amd/csrc/mhc.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "seam_T16384_hbm_counters.md")
 
 
