@@ -281,6 +281,7 @@ def main():
     del x, x_next, li, y
     torch.cuda.empty_cache()
     chain = None if args.no_sweep else run_chain(torch, M, mi, dev, bf, f32)
+    other = None if args.no_sweep else run_other_sizes(torch, M, mi, dev)
 
     M.check_default_workspaces(clear=False)
 
@@ -327,6 +328,7 @@ def main():
         "collapse": collapse,
         "pre_own": own,
         "seam_chain": chain,
+        "other_hidden_sizes": other,
     }
     print(json.dumps(line), flush=True)
 
@@ -444,6 +446,52 @@ def run_own(torch, M, x, w, ws):
     nbytes = pre_bytes(T, norm=False, delayed=False)
     return {"T": T, "us": round(us, 2), "alg_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "launches": 2}
+
+
+def run_other_sizes(torch, M, mi, dev, T=T_SEAM):
+    """The fused seam and the delayed pre at the other hidden sizes with a persistent
+    form (C = 4096 and 7168), T = 16384: inputs drawn on the device with torch's seeded
+    generator (x, y ~ N(0,1) bf16; gates: post = 2 sigmoid(N(0,1)), comb rows
+    normalised uniform, pre_in uniform), weights as the seam's; algorithmic GB/s and
+    the fraction of 8 TB/s per kernel."""
+    res = {}
+    for Cx in (4096, 7168):
+        g = torch.Generator(device=dev)
+        g.manual_seed(Cx)
+        x = torch.randn((T, NS, Cx), generator=g, device=dev).to(torch.bfloat16)
+        y = torch.randn((T, Cx), generator=g, device=dev).to(torch.bfloat16)
+        post_in = 2.0 * torch.sigmoid(torch.randn((T, NS), generator=g, device=dev))
+        comb_in = torch.rand((T, NS, NS), generator=g, device=dev)
+        comb_in = (comb_in / comb_in.sum(dim=-1, keepdim=True)).contiguous()
+        pre_in = torch.rand((T, NS), generator=g, device=dev)
+        fn, bias, alpha = mi.seam_weights(Cx, NS * Cx)
+        w = M.make_weights(torch.from_numpy(fn).to(dev), torch.from_numpy(bias).to(dev),
+                           torch.from_numpy(alpha).to(dev))
+        nw = (1.0 + 0.1 * torch.randn((Cx,), generator=g, device=dev)).to(torch.bfloat16)
+        ws = M.workspace(dev, T, Cx)
+        xo = torch.empty_like(x)
+        outs = M._pre_outputs(T, Cx, dev)
+        M.mhc_post_pre_delayed(y, x, post_in, comb_in, pre_in, w, nw, 1e-6, 20, out=(xo, *outs), ws=ws)
+        torch.cuda.synchronize()
+        f_us = _median_us(lambda n: [M.mhc_post_pre_delayed(y, x, post_in, comb_in, pre_in, w, nw, 1e-6, 20,
+                                                             out=(xo, *outs), ws=ws) for _ in range(n)],
+                          torch, reps=3, iters=20)
+        d_us = _median_us(lambda n: [M.mhc_pre_delayed(x, pre_in, w, nw, 1e-6, 20, out=outs, ws=ws)
+                                     for _ in range(n)], torch, reps=3, iters=20)
+        M.check_workspace(ws, clear=False)
+        fb, pb = fused_bytes(T, Cx), pre_bytes(T, Cx)
+        res[str(Cx)] = {
+            "T": T,
+            "fused": {"kernel": "mhc_persist_kernel<%d, true, false>" % Cx, "us": round(f_us, 2),
+                      "alg_GBps": round(fb / (f_us * 1e-6) / 1e9, 1),
+                      "frac": round(fb / (f_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+            "delayed": {"kernel": "mhc_persist_kernel<%d, false, false>" % Cx, "us": round(d_us, 2),
+                        "alg_GBps": round(pb / (d_us * 1e-6) / 1e9, 1),
+                        "frac": round(pb / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        }
+        del x, y, xo, outs
+        torch.cuda.empty_cache()
+    return res
 
 
 def run_chain(torch, M, mi, dev, bf, f32, n_seams=80):

@@ -39,14 +39,23 @@ constexpr int kMinKBPerSplit = 8;   // two 32-k steps per wave at least
 constexpr size_t kStreamBytes = (size_t)256 << 20;   // the memory-side cache (MALL) of MI355X
 constexpr int kMaxC = 16384;
 // The persistent kernels keep a tile's collapsed rows on chip and split each
-// 64-token tile over a group of 16 workgroups; they win once the split form's
+// 64-token tile over a group of workgroups; they win once the split form's
 // per-tile weight reads and duplicate residual reads (projection and collapse
-// workgroups) outweigh its parallelism.  Measured (graph replay, C = 5120):
-// delayed pre, split vs persistent, T = 1024: 21.0 vs 37.7 us, T = 4096: 63.9
-// vs 66.8 us, T = 8192: 177 vs 117 us; fused seam (the split kernel's fused
-// mode vs the persistent fused kernel), T = 1281: 36.2 vs 54.9
-// us, T = 2048: 55.0 vs 59.7 us, T = 3072: 79.6 vs 94.2 us, T = 4096: 135.7 vs
-// 118.3 us; delayed pre at T = 4160: 83.1 vs 73.8 us.
+// workgroups) outweigh its parallelism.  Measured (eager, back to back, split
+// vs persistent, microseconds):
+//   C = 5120  delayed  T = 4096: 62.9 vs 67.5, 4608: 84.5 vs 68.3, 8192: 172.6 vs 117.0
+//             own      T = 4096: 78.3 vs 91.2, 4608: 116.2 vs 95.5, 16384: 355.7 vs 283.4
+//             fused    T = 3072: 81.8 vs 88.3, 3584: 125.3 vs 99.0 (two launches vs one)
+//   C = 4096  delayed  T = 4096: 59.9 vs 63.9, 4608: 72.9 vs 63.3
+//             own      T = 4096: 72.9 vs 81.0, 4608: 102.5 vs 84.4
+//             fused    T = 3072: 64.4 vs 71.4, 3584: 99.7 vs 81.4
+//   C = 7168  delayed  T = 3584: 76.0 vs 83.6, 4096: 98.3 vs 99.5, 4608: 131.3 vs 107.2
+//             own      T = 2048: 95.0 vs 77.1, 3072: 108.4 vs 101.6
+//             fused    T = 2048: 79.1 vs 81.8, 3072: 144.7 vs 121.3
+// The own-pre-mix persistent form is the gates-only pass, then the collapse
+// kernel with the seam's pre-mix (a second pass over x, which this form needs
+// anyway); its split form is one workgroup per 16-token tile collapsing its
+// tokens after the gates.
 // Hidden sizes with a persistent form, and the workgroups of one group (the
 // member count: each member's weight slice must fit in LDS).
 int persist_pg(int C) {
@@ -57,15 +66,10 @@ int persist_pg(int C) {
     default: return 0;
   }
 }
-constexpr int kDelayedSplitMaxT = 4096;  // delayed pre: split form up to here, persistent beyond
-// Own pre-mix (mhc_pre), many tokens: the persistent kernel's gates-only form,
-// then the collapse kernel with the seam's pre-mix (a second pass over x, which
-// this form needs anyway), against the split kernel without splits (one
-// workgroup per 16-token tile collapsing its tokens after the gates): T = 4608
-// 85.7 vs 112.3 us, T = 8192 154 vs 175 us, T = 16384 292 vs 346 us (T = 3072:
-// 68.0 vs 65.1 us, T = 6144: 119.8 vs 110.5 us).
-constexpr int kOwnSplitMaxT = 4096;
-constexpr int kFusedGroupSplitMaxT = 3072;  // fused seam: the same threshold
+// The largest token counts that run the split form; persistent beyond.
+constexpr int kDelayedSplitMaxT = 4096;
+int own_split_max_t(int C) { return C >= 7168 ? 2048 : 4096; }
+int fused_group_split_max_t(int C) { return C >= 7168 ? 2048 : 3072; }
 // Fused seam below the persistent form: the split kernel's fused mode (one
 // launch) against the post kernel followed by the delayed split kernel, T =
 // 16: 10.8 vs 11.9 us, T = 128: 14.5 vs 18.0 us, T = 1024: 32.1 vs 41.7 us.
@@ -80,16 +84,16 @@ struct Plan {
 };
 
 // form: kModePre / kModeEntry (own pre-mix), kModeDelayed or kModeFused;
-// pg: group size of the persistent kernels for this hidden size (0: none).
-Plan make_plan(int T, int KB, int form, int pg) {
+// C: the hidden size; pg: group size of the persistent kernels for this hidden size (0: none).
+Plan make_plan(int T, int C, int KB, int form, int pg) {
   Plan pl;
   const bool persist_ok = pg > 0;
   pl.pg = pg;
   pl.ntile = (T + kTileT - 1) / kTileT;
   const bool delayed = form == kModeDelayed || form == kModeFused;
   pl.persist = persist_ok && ((form == kModeDelayed && T > kDelayedSplitMaxT) ||
-                              (form == kModeFused && T > kFusedGroupSplitMaxT) ||
-                              (form == kModePre && T > kOwnSplitMaxT));
+                              (form == kModeFused && T > fused_group_split_max_t(C)) ||
+                              (form == kModePre && T > own_split_max_t(C)));
   int ns = pl.persist ? 1 : splits_for(pl.ntile, delayed);
   int maxs = KB / kMinKBPerSplit;
   if (maxs < 1) maxs = 1;
@@ -326,7 +330,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
     if ((st = scratch_of(static_cast<hipStream_t>(stream), &ws)) != MHC_OK) return st;
     ws_bytes = kScratchBytes;
   }
-  Plan pl = make_plan(T, KB, mode, entry ? 0 : persist_pg(C));
+  Plan pl = make_plan(T, C, KB, mode, entry ? 0 : persist_pg(C));
   const size_t need = plan_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return MHC_ERR_WORKSPACE;
 
@@ -409,7 +413,7 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
       return launched();
     }
     // a device too small for one group: the split form (its workspace need is covered)
-    pl = make_plan(T, KB, mode, 0);
+    pl = make_plan(T, C, KB, mode, 0);
     p.ntile = pl.ntile;
     p.nsplit = pl.nsplit;
     p.nproj = pl.nproj;
@@ -464,14 +468,14 @@ size_t mhc_workspace_bytes(int T_max, int n, int C) {
   for (int KB : KBs) {
     for (int nt = 1; nt <= ntile_max && nt <= kMaxSplitTiles; ++nt) {
       for (int form : {kModePre, kModeDelayed, kModeFused}) {
-        const Plan pl = make_plan(nt * kTileT, KB, form, 0);
+        const Plan pl = make_plan(nt * kTileT, C, KB, form, 0);
         const size_t b = plan_ws_bytes(pl);
         if (b > best) best = b;
       }
     }
   }
   // the persistent forms: fixed size
-  const int persist_min_t = std::min(std::min(kFusedGroupSplitMaxT, kDelayedSplitMaxT), kOwnSplitMaxT) + 1;
+  const int persist_min_t = std::min(std::min(fused_group_split_max_t(C), kDelayedSplitMaxT), own_split_max_t(C)) + 1;
   const int pg = persist_pg(C);
   if (pg > 0 && T_max >= persist_min_t && persist_ws_bytes(pg) > best) best = persist_ws_bytes(pg);
   return best;

@@ -577,7 +577,9 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
       // (fused: each output stream of the post stage at its own sub-step, from
       // opaque copies of the packed inputs -- sharing their unpacking across the
       // sub-steps would keep forty unpacked values live -- and the next line's
-      // loads once the raw inputs are used up)
+      // loads at the line's third sub-step, into the buffer the previous line
+      // freed: two sub-steps more lead than at its last, 1% faster at C = 5120,
+      // T = 16384; any earlier, C = 5120 runs out of registers)
       static_for<kNS>([&](auto sc) __attribute__((always_inline)) {
 #pragma clang fp contract(off)
         constexpr int s = decltype(sc)::value;
@@ -598,7 +600,7 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
           const float pw = s_g[wave][tok][s];
           const float4 c = *reinterpret_cast<const float4*>(&s_g[wave][tok][4 + 4 * s]);
           xv = post_packed8(pw, c.x, c.y, c.z, c.w, in[0], in[1], in[2], in[3], in[4]);
-          if constexpr (s == kNS - 1) refill();
+          if constexpr (s == 2) refill();
           buf_store16(xv, rxo, xls[s] + u * 128, mcol);
         } else {
           xv = xq[(kNS * (P * kL + u) + s) % kRing];

@@ -41,3 +41,6 @@ def test_algorithmic_bytes():
     assert bench.fused_bytes(16384) == 16384 * 102_592 + 1_976_428
     # entry: h in, four-stream residual, layer_input and gates out; the narrower weight
     assert bench.entry_bytes(1) == 10_240 + 40_960 + 10_240 + 96 + 491_520 + 108 + 10_240
+    # other hidden sizes: 20 C + 192 bytes per token, 96 (4 C) + 108 + 2 C per call
+    assert bench.fused_bytes(16384, 7168) == 16384 * 143_552 + 2_766_956
+    assert bench.fused_bytes(16384, 4096) == 16384 * 82_112 + 1_581_164

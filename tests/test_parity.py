@@ -788,11 +788,14 @@ def test_config4_seam_chain_sampled(T):
 
 # ----------------------------------------------------------------------------- other hidden sizes
 
-@pytest.mark.parametrize("Cx,T", [(7168, 4100), (4096, 3100), (4096, 4100)])
+@pytest.mark.parametrize("Cx,T", [(7168, 2100), (7168, 4100), (7168, 6001), (4096, 3100), (4096, 4100),
+                                  (4096, 6001)])
 def test_other_hidden_sizes_many_tokens(Cx, T):
-    """Other hidden sizes at token counts past the decode sizes, every token: the
-    fused seam (its x_out bit for bit equal to mhc_post's), the delayed pre and the
-    own pre-mix form against the oracle."""
+    """Other hidden sizes with a persistent form (4096, 7168) at token counts past the
+    decode sizes, every token: the fused seam (its x_out bit for bit equal to
+    mhc_post's), the delayed pre and the own pre-mix form against the oracle.  At
+    C = 7168 the fused and own forms are persistent from T = 2049, the delayed form
+    from T = 4097 (at C = 4096: 3073 and 4097)."""
     torch = torch_mod()
     d = mi.pre_inputs(T, seed=2200 + Cx + T, C=Cx, delayed=True, norm=True, outlier_frac=0.01)
     say("hidden %d T=%d" % (Cx, T))
