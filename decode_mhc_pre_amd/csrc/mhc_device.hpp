@@ -96,6 +96,10 @@ __device__ __forceinline__ uint4 buf_load16_nt(rsrc_t r, int voff, int soff) {
 __device__ __forceinline__ void buf_store16(uint4 v, rsrc_t r, int voff, int soff) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
 }
+// streaming (non-temporal) variant for data written once and not read back by this call
+__device__ __forceinline__ void buf_store16_nt(uint4 v, rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 2);
+}
 
 // ---------------------------------------------------------------- device-coherent access
 // Values passed between workgroups (which may sit on different XCDs, each with

@@ -77,6 +77,7 @@ def test_noalloc_graph_replays():
     for T in (1, 5000):
         say("noalloc graph T=%d" % T)
         args = _inputs(T, C, seed=T)
+        torch.cuda.synchronize()   # the inputs were drawn on the default stream; the calls run on s
         with torch.cuda.stream(s):
             out = [torch.empty_like(args[1])] + list(M._pre_outputs(T, C, args[1].device))
             M.mhc_post_pre_delayed_noalloc(*args, w, nw, 1e-6, 20, out=out)
