@@ -125,6 +125,14 @@ __device__ __forceinline__ void buf_store16_agent(uint4 v, rsrc_t r, int voff, i
 // included); also a compiler barrier for memory.
 __device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// ---------------------------------------------------------------- gate arithmetic
+// The hardware's exponential, reciprocal and reciprocal square root (each within
+// about 1 ulp; exp(x) as 2^(x log2 e), whose product adds |x| 2^-24 relative).
+// The gates' error budget is 1e-4 relative; these keep the gate set-up short.
+__device__ __forceinline__ float hw_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float hw_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float hw_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + hw_exp(-x)); }
+
 // ---------------------------------------------------------------- quad shuffles (DPP)
 // Lane l reads lane l^1 / l^2 of its quad; all 64 lanes must be active.
 __device__ __forceinline__ float dpp_quad_xor1(float v) {

@@ -98,9 +98,10 @@ __global__ __launch_bounds__(256) void mhc_pack_fn_kernel(const float* __restric
 // the 16-lane row by 8 (the same as exchanging with lane ^ 8) and then by 4,
 // which pairs (0,2) and (1,3) in every lane.  Either way every lane of a row
 // or column divides by the same bits.  The row maximum is subtracted before
-// exp (removed exactly by the first row step); reciprocals are the hardware's
-// (error <= 1 ulp).  The lanes of row 0 also make the token's pre and post
-// gates (gate index j).  `ba` holds bias[24] then alpha[3] (LDS).
+// exp (removed exactly by the first row step); reciprocals, the exponential and
+// the reciprocal square root are the hardware's (about 1 ulp each).  The lanes of
+// row 0 also make the token's pre and post gates (gate index j).  `ba` holds
+// bias[24] then alpha[3] (LDS).
 // `rec` (or nullptr): the own-pre-mix records the tile's collapse workgroups wait on.
 __device__ __forceinline__ void tile_gates(const PreParams& p, const float* ba, const float (*s_P)[kPS], int t0,
                                            float (*s_pre)[kNS], unsigned* rec) {
@@ -110,11 +111,11 @@ __device__ __forceinline__ void tile_gates(const PreParams& p, const float* ba, 
   const int j = lane & 3;
   const int tk = t0 + tt;
   const bool ok = tk < p.T;
-  const float r = 1.0f / sqrtf(s_P[tt][24] / (float)p.K + p.eps);
+  const float r = hw_rsqrt(s_P[tt][24] * (1.0f / (float)p.K) + p.eps);
   float m = ba[kNL + 2] * (r * s_P[tt][8 + 4 * i + j]) + ba[8 + 4 * i + j];
   float mx = fmaxf(m, dpp_quad_xor1(m));
   mx = fmaxf(mx, dpp_quad_xor2(mx));
-  m = expf(m - mx);
+  m = hw_exp(m - mx);
   for (int it = 0; it < p.iters; ++it) {
     float rs = m + dpp_quad_xor1(m);
     rs = rs + dpp_quad_xor2(rs);
@@ -126,8 +127,8 @@ __device__ __forceinline__ void tile_gates(const PreParams& p, const float* ba, 
   if (i == 0) {
     const float lp = ba[kNL] * (r * s_P[tt][j]) + ba[j];
     const float lq = ba[kNL + 1] * (r * s_P[tt][4 + j]) + ba[4 + j];
-    const float pr = 1.0f / (1.0f + expf(-lp));
-    const float po = 2.0f / (1.0f + expf(-lq));
+    const float pr = hw_sigmoid(lp);
+    const float po = 2.0f * hw_sigmoid(lq);
     s_pre[tt][j] = pr;
     if (ok) {
       p.pre[(size_t)tk * kNS + j] = pr;
@@ -217,7 +218,7 @@ __device__ __forceinline__ void collapse_norm_token(const PreParams& p, int tok,
   }
   if (!norm || (kBcast && p.li == nullptr)) return;
   const float tot = block_sum(ss, s_tmp);
-  const float ry = 1.0f / sqrtf(tot / (float)p.C + p.eps);
+  const float ry = hw_rsqrt(tot * (1.0f / (float)p.C) + p.eps);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int c8 = threadIdx.x + s * kThreads;
@@ -301,7 +302,7 @@ __device__ __forceinline__ void collapse_token_wave(const PreParams& p, int tok,
   }
   if (!norm || (kBcast && p.li == nullptr)) return;
   const float tot = wave_sum(ss);
-  const float ry = 1.0f / sqrtf(tot / (float)p.C + p.eps);
+  const float ry = hw_rsqrt(tot * (1.0f / (float)p.C) + p.eps);
 #pragma unroll
   for (int ch = 0; ch < kCh; ++ch) {
     const int c8 = lane + ch * kWave;
@@ -401,7 +402,7 @@ __device__ __forceinline__ void collapse_own_token(const PreParams& p, int tok, 
   }
   if (!norm) return;
   const float tot = block_sum(ss, s_tmp);
-  const float ry = 1.0f / sqrtf(tot / (float)p.C + p.eps);
+  const float ry = hw_rsqrt(tot * (1.0f / (float)p.C) + p.eps);
   const uint4* w8 = reinterpret_cast<const uint4*>(p.nw);
 #pragma unroll
   for (int s = 0; s < kCh; ++s) {

@@ -135,7 +135,7 @@ struct TokenGates {
   __device__ __forceinline__ void init_a(const PreParams& p, const float* v, const float* ba, int t,
                                          bool w, int lane) {
     const int row = lane & 3;
-    const float r = 1.0f / sqrtf(v[24] / (float)p.K + p.eps);
+    const float r = hw_rsqrt(v[24] * (1.0f / (float)p.K) + p.eps);
     const float ac = ba[kNL + 2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) m[j] = ac * (r * v[8 + 4 * row + j]) + ba[8 + 4 * row + j];
@@ -148,11 +148,11 @@ struct TokenGates {
   __device__ __forceinline__ void init_b() {
     const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] = expf(m[j] - mx);
+    for (int j = 0; j < 4; ++j) m[j] = hw_exp(m[j] - mx);
   }
   __device__ __forceinline__ void init_c() {
-    pr = 1.0f / (1.0f + expf(-pr));
-    po = 2.0f / (1.0f + expf(-po));
+    pr = hw_sigmoid(pr);
+    po = 2.0f * hw_sigmoid(po);
   }
   // one Sinkhorn iteration, if this wave holds a gate token with iterations left
   __device__ __forceinline__ void step(int iters) {
@@ -237,9 +237,15 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
   const int grp = blockIdx.x / kPG;
   const int ntiles = (p.T + kPT - 1) / kPT;
   const int nk = (ntiles - 1 - grp) / ngroups + 1;   // tiles of this group (launch: ngroups <= ntiles)
-  const int mcol = kL * 128 * mem;                   // byte offset of the member's first line in a row (SGPR)
-  const int xlane = (wave * kPTW + tok) * kRow + chunk * 16;
-  int ylane = (wave * kPTW + tok) * kYRow + chunk * 16;
+  const int mcol = kL * 128 * mem;                   // byte offset of the member's first line in a row
+  // The member's column offset is part of the lane offsets, and every buffer
+  // access passes a literal zero as its scalar offset: the compiler inserts the
+  // wait state a 16-byte store needs before its data registers are written again
+  // only for stores without a scalar offset register, and on gfx950 a store with
+  // one showed the hazard (a move into a store's first data register right after
+  // it changed what the store wrote in lanes 12-15 of each 16).
+  const int xlane = (wave * kPTW + tok) * kRow + chunk * 16 + mcol;
+  int ylane = (wave * kPTW + tok) * kYRow + chunk * 16 + mcol;
   // lane offset of each stream (the line offset, at most 4 x 128 bytes, fits the
   // instructions' immediate field; opaque, so the compiler forms base + constant
   // at each access instead of keeping one register per (stream, line))
@@ -289,8 +295,8 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
   uint4 ra[kRaw], rb[kRaw];
   auto issue_line = [&](uint4 (&r)[kRaw], rsrc_t rx, rsrc_t ryy, int u) {
 #pragma unroll
-    for (int s = 0; s < kNS; ++s) r[s] = buf_load16(rx, xls[s] + u * 128, mcol);
-    if constexpr (kFused) r[4] = buf_load16(ryy, ylane + u * 128, mcol);
+    for (int s = 0; s < kNS; ++s) r[s] = buf_load16(rx, xls[s] + u * 128, 0);
+    if constexpr (kFused) r[4] = buf_load16(ryy, ylane + u * 128, 0);
   };
   // the gates a tile needs for the wave's eight tokens, one 16-byte load per
   // lane: pre_in rows to lanes 0-7, (fused) post_in rows to lanes 8-15 and
@@ -324,7 +330,7 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
     for (int g = 0; g < kRing; ++g) {
       const int u = g / kNS;
       const int t = tile_of(u / kL);
-      xq[g] = buf_load16(x_rsrc(t), xls[g % kNS] + (u % kL) * 128, mcol);
+      xq[g] = buf_load16(x_rsrc(t), xls[g % kNS] + (u % kL) * 128, 0);
     }
   }
   issue_gates(tile_of(0));
@@ -506,7 +512,7 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
       for (int e = 0; e < 4; ++e) g[e] += xshfl(g[e], m);
     if (lane < 8) *reinterpret_cast<float4*>(&s_gv[wave][4 * lane]) = make_float4(g[0], g[1], g[2], g[3]);
     const float sy = s_ry[wave][tok];
-    ry = norm ? 1.0f / sqrtf(sy / (float)kC + p.eps) : 1.0f;
+    ry = norm ? hw_rsqrt(sy * (1.0f / (float)kC) + p.eps) : 1.0f;
   };
   // one line of layer_input from a row buffer (non-temporal, as the next residual:
   // 3% off the delayed pre and 1% off the fused seam at T = 16384, C = 5120; the
@@ -523,7 +529,7 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = yb[e];
     }
-    buf_store16_nt(pack8(o), rl, ylane + u * 128, mcol);
+    buf_store16_nt(pack8(o), rl, ylane + u * 128, 0);
   };
 
   // One tile: the sweep of the group's k-th tile into yb (which held tile k - 2:
@@ -604,7 +610,7 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
           const float4 c = *reinterpret_cast<const float4*>(&s_g[wave][tok][4 + 4 * s]);
           xv = post_packed8(pw, c.x, c.y, c.z, c.w, in[0], in[1], in[2], in[3], in[4]);
           if constexpr (s == 2) refill();
-          buf_store16_nt(xv, rxo, xls[s] + u * 128, mcol);
+          buf_store16_nt(xv, rxo, xls[s] + u * 128, 0);
         } else {
           xv = xq[(kNS * (P * kL + u) + s) % kRing];
         }
@@ -639,7 +645,7 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
           constexpr int g = kNS * (P * kL + u) + s;
           constexpr int un = u + 2;   // line of the refill, counted from this tile's first
           const rsrc_t rr = un < kL ? rx : rxn;
-          xq[g % kRing] = buf_load16(rr, xls[s] + (un % kL) * 128, mcol);
+          xq[g % kRing] = buf_load16(rr, xls[s] + (un % kL) * 128, 0);
         }
         // ---- exchange of tile k - 1, continued
         if constexpr (ss == kArrive) {
