@@ -37,16 +37,18 @@
 // written at the start of tile k + 1 (one whole-line store per wave); a load
 // issued right after those stores (a wave's vector memory operations complete
 // in issue order) tells when they are complete, and the arrival is counted
-// then.  Late in tile k + 1 the wave checks that every member arrived and
-// reads the records back: the sum-y^2 block (norm factors, every member) and
-// its gate token's lines (members 0-7 take the wave's tokens 0-7 of even
-// tiles, members 8-15 those of odd tiles: gates, then one Sinkhorn iteration
-// per sub-step of tile k + 2).  Tile k's layer_input is written during tile
-// k + 2, each line just before the sweep overwrites its row buffer, so two row
-// buffers give the exchange more than a tile of slack.  Record slots alternate
-// (slot k % 2 is rewritten at the start of tile k + 2, after its writer saw
-// every member arrive for tile k + 1, which each does after consuming tile k's
-// records).
+// then.  Late in tile k + 1 the wave checks that every member arrived (the
+// counter read a few sub-steps before) and issues the loads of the records:
+// the sum-y^2 block (norm factors, every member) and its gate token's lines
+// (members 0-7 take the wave's tokens 0-7 of even tiles, members 8-15 those
+// of odd tiles).  They are summed at the start of tile k + 2, whose sub-steps
+// then run the gate token's gates and one Sinkhorn iteration each.  Tile k's
+// layer_input is written during tile k + 2, each line just before the sweep
+// overwrites its row buffer, so two row buffers give the exchange more than a
+// tile of slack.  Record slots alternate (slot k % 2 is rewritten at the start
+// of tile k + 2, after its writer saw every member arrive for tile k + 1,
+// which each does after its loads of tile k's records are back: they were
+// issued before the fence load that the arrival waits for).
 //
 // Forward progress: a group is kPG consecutive blocks, dispatched in order, so
 // groups become resident whole or behind groups that are; those finish all of
@@ -204,18 +206,20 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
   static_assert(kPG <= kPMaxPG && kPG >= kPTW, "every token of a wave needs a gate member");
   static_assert(!(kFused && kGates), "the gates-only form has no post stage");
   static_assert((kFrags * kWave) % kPThreads == 0, "weight fragments split evenly over the threads");
-  // exchange sub-steps of tile k for tile k - 1 (counted in stream loads, 4 per line)
-  // (the check as late as the tile allows: tile k - 1's norm factors are first
-  // needed at the start of tile k + 1, and every sub-step between the arrival
-  // and the check is slack for members that run behind)
+  // exchange sub-steps (counted in stream loads, 4 per line).  In tile k, for
+  // tile k - 1: the arrival, the counter read and, late, the check and the
+  // record loads (every sub-step between the arrival and the check is slack for
+  // members that run behind); the loads are summed at the start of tile k + 1,
+  // so that the wait for them has several sub-steps of loads in flight in front
+  // of it.  In tile k, for tile k - 2: its records summed (norm factors, gate
+  // token's values), then its gate token's gates and Sinkhorn iterations.
   constexpr int kArrive = 2;                    // the fence load issued after the record stores is back
   constexpr int kCntRead = kSS - 7;
   constexpr int kCheck = kSS - 4;
-  constexpr int kStage = kSS - 2;
-  constexpr int kInit = kSS - 1;                // gates of tile k - 1's token: logits, exponentials, gates
-  constexpr int kGateEnd = kInit - 1;           // tile k - 2's token: remaining iterations, written
-  constexpr int kIter = kSS;                    // (no iterations in the tile of the init)
-  static_assert(kCntRead > kArrive + 2 && kInit < kSS, "exchange schedule");
+  constexpr int kStage = 0;                     // tile k - 2's records summed, before its layer_input
+  constexpr int kInit = 1;                      // its gate token: logits, exponentials, gates
+  constexpr int kGateEnd = kSS - 2;             // its remaining iterations, written
+  static_assert(kCntRead > kArrive + 2 && kCheck < kSS && kGateEnd > kInit + 1, "exchange schedule");
 
   __shared__ uint4 s_w[kFrags * kWave];         // [line][stream][fragment][lane]
   __shared__ uint4 s_nw[kL * 8];                // the member's columns of the norm weight
@@ -369,7 +373,7 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
   float ybA[kL][8], ybB[kL][8];   // collapsed rows: tiles of even / odd index in the group
   float ryA = 1.f, ryB = 1.f;     // their norm factors, once known
   uint4 pssy = make_uint4(0u, 0u, 0u, 0u);   // tile k - 1's sum-y^2 block, in flight
-  uint4 pg[4];                               // the gate token's lines, in flight
+  uint4 pg[4] = {};                          // the gate token's lines, in flight
   unsigned cv = 0;
   TokenGates gt;
   gt.m[0] = gt.m[1] = gt.m[2] = gt.m[3] = 1.0f;
@@ -533,11 +537,10 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
   };
 
   // One tile: the sweep of the group's k-th tile into yb (which held tile k - 2:
-  // its layer_input leaves line by line just before the line is overwritten),
-  // and the exchange of tile k - 1 (norm factor into ry_prev).  P: the tile's
-  // parity (which raw-load buffer each line uses).
-  auto tile_body = [&](auto par, int k, float (&yb)[kL][8], float& ry_old, float& ry_prev)
-                       __attribute__((always_inline)) {
+  // its norm factor into ry at the start, then its layer_input leaves line by
+  // line just before the line is overwritten), and the exchange of tile k - 1.
+  // P: the tile's parity (which raw-load buffer each line uses).
+  auto tile_body = [&](auto par, int k, float (&yb)[kL][8], float& ry) __attribute__((always_inline)) {
 #pragma clang fp contract(off)
     constexpr int P = decltype(par)::value;
     // re-define the base offsets and lane indices in every tile (see xls, fb0, fb1, lane)
@@ -550,7 +553,7 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
     const rsrc_t rxn = x_rsrc(tn), ryn = y_rsrc(tn);
     const rsrc_t rxo = xo_rsrc(t);
     const rsrc_t rl2 = li_rsrc(tile_of(k - 2));   // zero bytes for k < 2: stores dropped
-    const int tp = tile_of(k - 1);                   // -1 for k = 0
+    const int tq = tile_of(k - 2);                   // -1 for k < 2
     // ---- exchange of tile k - 1: partial sums out, before the next line's loads
     publish_a();
 #pragma unroll
@@ -596,11 +599,14 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
         // keep each sub-step's weight reads, matrix instructions and collapse
         // together (hoisting a whole line's fragment reads would spill)
         __builtin_amdgcn_sched_barrier(0);
+        // tile k - 2's records (loaded during tile k - 1): its norm factor, first
+        // needed just below, and its gate token's values
+        if constexpr (ss == kStage) sum_records(ry);
         // Sinkhorn of tile k - 2's gate token: one iteration per sub-step
-        if constexpr (ss < kGateEnd || ss >= kIter) gt.step(p.iters);
+        if constexpr (ss > kInit && ss < kGateEnd) gt.step(p.iters);
         if constexpr (ss == kGateEnd) gt.finish(p, lane);
         // tile k - 2's layer_input for this line, before the line's first write
-        if constexpr (!kGates && s == 0) li_store(yb[u], ry_old, rl2, u);
+        if constexpr (!kGates && s == 0) li_store(yb[u], ry, rl2, u);
         uint4 xv;
         if constexpr (kFused) {
           uint4 in[5] = {rc[4], rc[0], rc[1], rc[2], rc[3]};
@@ -664,10 +670,9 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
           load_records(k - 1);
           __asm__ volatile("" ::: "memory");
         }
-        if constexpr (ss == kStage) sum_records(ry_prev);
         if constexpr (ss == kInit) {
-          gt.init_a(p, s_gv[wave], s_ba, tp * kPT + wave * kPTW + gate_tok(k - 1),
-                    tp >= 0 && gate_tok(k - 1) >= 0 && gate_tok(k - 1) < kPTW, lane);
+          gt.init_a(p, s_gv[wave], s_ba, tq * kPT + wave * kPTW + gate_tok(k - 2),
+                    tq >= 0 && gate_tok(k - 2) >= 0 && gate_tok(k - 2) < kPTW, lane);
           gt.init_b();
           gt.init_c();
         }
@@ -679,20 +684,26 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
     stage_gates();
   };
 
-  // After the last tile kl: its partial sums out, tile kl - 1's layer_input
-  // (norm factor known), then tile kl's exchange, gates and layer_input.
-  auto drain = [&](int kl, float (&ylast)[kL][8], float (&yprev)[kL][8], float ry_prev_of_last, float& ry_last) {
+  // After the last tile kl: its partial sums out; tile kl - 1's records (loaded
+  // during tile kl): norm factor, gates and layer_input; then tile kl's
+  // exchange, gates and layer_input.
+  auto drain = [&](int kl, float (&ylast)[kL][8], float (&yprev)[kL][8], float& ry_prev, float& ry_last) {
     publish_a();
     publish_b(kl);
-    wait_vmem();   // tile kl's records are stored
+    wait_vmem();   // tile kl's records are stored, tile kl - 1's are loaded
     if (lane == 0) __hip_atomic_fetch_add(cnt_of(kl), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!kGates && kl >= 1) {
-      const rsrc_t rl = li_rsrc(tile_of(kl - 1));
-#pragma unroll
-      for (int u = 0; u < kL; ++u) li_store(yprev[u], ry_prev_of_last, rl, u);
-    }
-    // tile kl - 1's gate token was set up during tile kl
+    sum_records(ry_prev);
+    const int tq = tile_of(kl - 1);
+    gt.init_a(p, s_gv[wave], s_ba, tq * kPT + wave * kPTW + gate_tok(kl - 1),
+              tq >= 0 && gate_tok(kl - 1) >= 0 && gate_tok(kl - 1) < kPTW, lane);
+    gt.init_b();
+    gt.init_c();
     gt.finish(p, lane);
+    if (!kGates && kl >= 1) {
+      const rsrc_t rl = li_rsrc(tq);
+#pragma unroll
+      for (int u = 0; u < kL; ++u) li_store(yprev[u], ry_prev, rl, u);
+    }
     const unsigned v = ld_agent(cnt_of(kl));
     if ((int)(v - target_of(kl)) < 0) wait_count(cnt_of(kl), target_of(kl), v);
     load_records(kl);
@@ -714,8 +725,8 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
   // two tile bodies (the row buffers alternate; each body's code stays small
   // enough for the instruction cache)
   for (int k = 0; k < nk; k += 2) {
-    tile_body(std::integral_constant<int, 0>(), k, ybA, ryA, ryB);
-    if (k + 1 < nk) tile_body(std::integral_constant<int, 1>(), k + 1, ybB, ryB, ryA);
+    tile_body(std::integral_constant<int, 0>(), k, ybA, ryA);
+    if (k + 1 < nk) tile_body(std::integral_constant<int, 1>(), k + 1, ybB, ryB);
   }
   if ((nk - 1) % 2 == 0)
     drain(nk - 1, ybA, ybB, ryB, ryA);
