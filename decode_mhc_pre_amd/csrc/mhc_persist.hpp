@@ -125,10 +125,13 @@ __device__ __forceinline__ unsigned zero_after(unsigned v) {
 
 // Gates and Sinkhorn of one token, in pieces.  The token's 25 summed values
 // (P[24], sum x^2) sit in `v`; `ba` holds bias[24] then alpha[3] (both LDS).
-// Every quad of the wave computes the same token (lane & 3 = comb row); the
-// quad of lanes 0-3 writes.
+// Each 16-lane DPP row of the wave holds the token's 4x4 comb matrix, lane
+// 4i + j entry (i, j) (the four rows compute the same): row sums by quad
+// butterflies, column sums by rotating the row by 8 and then by 4, so every
+// lane of a row or column divides by the same bits.  Lanes 0-15 write comb,
+// lanes 0-3 the pre and post gates (gate index j).
 struct TokenGates {
-  float m[4];
+  float m;
   float pr, po;
   int tok, it;
   bool write;
@@ -136,49 +139,47 @@ struct TokenGates {
   // in three pieces (each a short dependent chain): logits, exponentials, gates
   __device__ __forceinline__ void init_a(const PreParams& p, const float* v, const float* ba, int t,
                                          bool w, int lane) {
-    const int row = lane & 3;
+    const int e = lane & 15;       // 4 i + j
+    const int j = lane & 3;
     const float r = hw_rsqrt(v[24] * (1.0f / (float)p.K) + p.eps);
-    const float ac = ba[kNL + 2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] = ac * (r * v[8 + 4 * row + j]) + ba[8 + 4 * row + j];
-    pr = ba[kNL] * (r * v[row]) + ba[row];          // the pre logit, until init_c
-    po = ba[kNL + 1] * (r * v[4 + row]) + ba[4 + row];
+    m = ba[kNL + 2] * (r * v[8 + e]) + ba[8 + e];
+    pr = ba[kNL] * (r * v[j]) + ba[j];          // the pre logit, until init_c
+    po = ba[kNL + 1] * (r * v[4 + j]) + ba[4 + j];
     tok = t;
     it = 0;
     write = w;
   }
   __device__ __forceinline__ void init_b() {
-    const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] = hw_exp(m[j] - mx);
+    float mx = fmaxf(m, dpp_quad_xor1(m));
+    mx = fmaxf(mx, dpp_quad_xor2(mx));
+    m = hw_exp(m - mx);
   }
   __device__ __forceinline__ void init_c() {
     pr = hw_sigmoid(pr);
     po = 2.0f * hw_sigmoid(po);
   }
-  // one Sinkhorn iteration, if this wave holds a gate token with iterations left
+  // one Sinkhorn iteration (row normalisation, then column), if this wave holds a
+  // gate token with iterations left
   __device__ __forceinline__ void step(int iters) {
     if (write && it < iters) {
-      const float inv = __builtin_amdgcn_rcpf((m[0] + m[1]) + (m[2] + m[3]));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) m[j] *= inv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float c = m[j] + dpp_quad_xor1(m[j]);
-        c = c + dpp_quad_xor2(c);
-        m[j] *= __builtin_amdgcn_rcpf(c);
-      }
+      float rs = m + dpp_quad_xor1(m);
+      rs = rs + dpp_quad_xor2(rs);
+      m *= __builtin_amdgcn_rcpf(rs);
+      float cs = m + dpp_row_ror8(m);
+      cs = cs + dpp_row_ror4(cs);
+      m *= __builtin_amdgcn_rcpf(cs);
       ++it;
     }
   }
   __device__ __forceinline__ void finish(const PreParams& p, int lane) {
     if (!write) return;
     while (it < p.iters) step(p.iters);
-    const int row = lane & 3;
-    if (lane < 4 && tok < p.T) {
-      reinterpret_cast<float4*>(p.comb)[(size_t)tok * 4 + row] = make_float4(m[0], m[1], m[2], m[3]);
-      p.pre[(size_t)tok * kNS + row] = pr;
-      p.post[(size_t)tok * kNS + row] = po;
+    if (lane < 16 && tok < p.T) {
+      p.comb[(size_t)tok * 16 + lane] = m;
+      if (lane < 4) {
+        p.pre[(size_t)tok * kNS + lane] = pr;
+        p.post[(size_t)tok * kNS + lane] = po;
+      }
     }
     write = false;
   }
@@ -376,7 +377,7 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
   uint4 pg[4] = {};                          // the gate token's lines, in flight
   unsigned cv = 0;
   TokenGates gt;
-  gt.m[0] = gt.m[1] = gt.m[2] = gt.m[3] = 1.0f;
+  gt.m = 1.0f;
   gt.pr = gt.po = 0.0f;
   gt.tok = -1;
   gt.write = false;
