@@ -269,6 +269,7 @@ def main():
         del src, dst
     copy = copy_ceiling(torch, dev)
     copy["fused_frac_of_copy"] = round(kernels[dom]["gbs"] / copy["copy_GBps"], 4)
+    ceilings = memory_ceilings(torch, dev, x, y, x_next, li, fused_avg * 1e3, pre_avg * 1e3)
 
     # ---------------------------------------------------------------- T = 1..128 sweep
     sweep = None
@@ -315,6 +316,7 @@ def main():
         "cpu_baseline": cpu,
         "accuracy": accuracy,
         "copy_ceiling": copy,
+        "memory_ceilings": ceilings,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "kernel_timing": "fused step: one HIP event pair on the launch stream around the timed launches "
@@ -576,6 +578,80 @@ def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
     torch.cuda.empty_cache()
     return {"kind": "torch copy_ of 1 GiB (read + write)", "copy_GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(2 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def memory_ceilings(torch, dev, x, y, xo, li, fused_us, delayed_us, reps=10):
+    """What the memory system moves with no arithmetic, measured in the same run on
+    the step's own buffers (bench_ceilings.hip; xo and li are overwritten): streams of
+    16-byte non-temporal reads of x, writes of xo and a copy x -> xo; the floors they
+    give the fused seam's and the delayed pre's bulk bytes (reads and writes adding
+    up in time, R / read rate + W / write rate; and all bytes at the copy rate); and
+    the traffic of the persistent pre kernels' own access pattern replayed with no
+    arithmetic or exchange (same grid, tile walk, line loads and non-temporal
+    stores)."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_ceilings.so")
+    if not os.path.exists(path):
+        print("bench.py: bench_ceilings.so is not built (__graft_entry__.build() builds it); "
+              "memory ceilings not measured", file=sys.stderr, flush=True)
+        return {"skipped": "bench_ceilings.so not built"}
+    L = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.ceil_stream.argtypes = [I, P, P, Z, P, P]
+    L.ceil_pattern_run.argtypes = [I, P, P, P, P, I, I, P]
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    nbytes = x.numel() * x.element_size()
+
+    def run(fn, n):
+        for _ in range(3):
+            fn()
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(n):
+            fn()
+        e0.record(stream)
+        e0.synchronize()
+        return s0.elapsed_time(e0) * 1e3 / n   # us per call
+
+    def stream_rate(kind):
+        def fn():
+            rc = L.ceil_stream(kind, x.data_ptr(), xo.data_ptr(), nbytes, sink.data_ptr(), sp)
+            if rc != 0:
+                raise RuntimeError("ceil_stream(%d) returned %d" % (kind, rc))
+        moved = nbytes * (2 if kind == 2 else 1)
+        return moved / (run(fn, reps) * 1e-6) / 1e9
+
+    read_gbs, write_gbs, copy_gbs = stream_rate(0), stream_rate(1), stream_rate(2)
+    T = x.shape[0]
+    ng = max(1, min(16, torch.cuda.get_device_properties(dev).multi_processor_count // 16, (T + 63) // 64))
+
+    def pattern(fused):
+        def fn():
+            rc = L.ceil_pattern_run(int(fused), x.data_ptr(), y.data_ptr(), xo.data_ptr(), li.data_ptr(), T, ng, sp)
+            if rc != 0:
+                raise RuntimeError("ceil_pattern_run returned %d" % rc)
+        return run(fn, 20)
+
+    fused_pat, delayed_pat = pattern(True), pattern(False)
+    torch.cuda.synchronize()
+    K = NS * C
+    fr, fw = T * (C * 2 + K * 2), T * (K * 2 + C * 2)    # the fused seam's bulk reads / writes
+    dr, dw = T * K * 2, T * C * 2                        # the delayed pre's
+    floor_f = (fr / read_gbs + fw / write_gbs) / 1e3     # us
+    floor_d = (dr / read_gbs + dw / write_gbs) / 1e3
+    copy_f, copy_d = (fr + fw) / copy_gbs / 1e3, (dr + dw) / copy_gbs / 1e3
+    return {"kind": "16-byte non-temporal accesses over the step's residual buffers (%d MB); the pre kernels' "
+                    "access pattern replayed without arithmetic or exchange (T=%d, C=%d, %d groups of 16 "
+                    "workgroups)" % (nbytes // 1000000, T, C, ng),
+            "read_GBps": round(read_gbs, 1), "write_GBps": round(write_gbs, 1), "copy_GBps": round(copy_gbs, 1),
+            "fused_seam": {"kernel_us": round(fused_us, 1), "additive_floor_us": round(floor_f, 1),
+                           "copy_rate_floor_us": round(copy_f, 1), "pattern_probe_us": round(fused_pat, 1),
+                           "kernel_over_pattern": round(fused_us / fused_pat, 3)},
+            "delayed_pre": {"kernel_us": round(delayed_us, 1), "additive_floor_us": round(floor_d, 1),
+                            "copy_rate_floor_us": round(copy_d, 1), "pattern_probe_us": round(delayed_pat, 1),
+                            "kernel_over_pattern": round(delayed_us / delayed_pat, 3)}}
 
 
 def _cpu_model():

@@ -25,6 +25,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wno-pass-failed", "-I" + INCLUDE]
 
 
+# The benchmark's memory-ceiling probes (bench_ceilings.hip beside bench.py): not
+# part of the library, built with the same compiler and flags.
+CEIL_SRC = os.path.join(ROOT, "bench_ceilings.hip")
+CEIL_LIB = os.path.join(ROOT, "bench_ceilings.so")
+
+
 def stale() -> bool:
     if not os.path.exists(LIB):
         return True
@@ -45,5 +51,19 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_ceilings(verbose: bool = False) -> str:
+    tmp = CEIL_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-o", tmp, CEIL_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building bench_ceilings.so")
+    os.replace(tmp, CEIL_LIB)
+    return CEIL_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_ceilings(verbose=True))

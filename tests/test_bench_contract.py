@@ -44,3 +44,27 @@ def test_algorithmic_bytes():
     # other hidden sizes: 20 C + 192 bytes per token, 96 (4 C) + 108 + 2 C per call
     assert bench.fused_bytes(16384, 7168) == 16384 * 143_552 + 2_766_956
     assert bench.fused_bytes(16384, 4096) == 16384 * 82_112 + 1_581_164
+
+
+def test_ceiling_probe_library_exports():
+    """bench_ceilings.so (the benchmark's memory-ceiling probes, built by
+    __graft_entry__.build()) loads and exports its two entry points; argument
+    checks reject bad calls before any launch."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_ceilings.so")
+    if not os.path.exists(path):
+        import pytest
+        pytest.skip("bench_ceilings.so not built")
+    L = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.ceil_stream.argtypes = [I, P, P, Z, P, P]
+    L.ceil_pattern_run.argtypes = [I, P, P, P, P, I, I, P]
+    fake = ctypes.c_void_p(1 << 40)   # never dereferenced: every call below fails validation
+    assert L.ceil_stream(3, fake, fake, 16, fake, None) == -1          # unknown kind
+    assert L.ceil_stream(0, fake, fake, 15, fake, None) == -1          # not a multiple of 16
+    assert L.ceil_stream(0, None, fake, 16, fake, None) == -1          # read needs a source
+    assert L.ceil_stream(2, fake, None, 16, fake, None) == -1          # copy needs a destination
+    assert L.ceil_stream(1, fake, fake, 16, None, None) == -1          # no sink
+    assert L.ceil_pattern_run(1, fake, fake, fake, fake, 0, 16, None) == -1     # T < 1
+    assert L.ceil_pattern_run(1, fake, fake, fake, fake, 64, 17, None) == -1    # too many groups
+    assert L.ceil_pattern_run(1, fake, None, fake, fake, 64, 16, None) == -1    # fused needs y
