@@ -220,6 +220,18 @@ void launch_persist(int mode, const PreParams& p, int ng, hipStream_t s) {
     hipLaunchKernelGGL((mhc_persist_kernel<kC, false, true>), grid, block, 0, s, p, ng);
 }
 
+// the post kernel: one thread per (token, 8 hidden elements); when a wave's 64
+// threads always share one token (C / 8 a multiple of 64), the wave-token form
+void launch_post(const uint4* y, const uint4* x, const float* post, const float* comb, uint4* out, int T, int C8,
+                 hipStream_t s) {
+  const long long total = (long long)T * C8;
+  const unsigned grid = (unsigned)((total + kThreads - 1) / kThreads);
+  if (C8 % kWave == 0)
+    hipLaunchKernelGGL(mhc_post_kernel<true>, dim3(grid), dim3(kThreads), 0, s, y, x, post, comb, out, T, C8);
+  else
+    hipLaunchKernelGGL(mhc_post_kernel<false>, dim3(grid), dim3(kThreads), 0, s, y, x, post, comb, out, T, C8);
+}
+
 // ------------------------------------------------------------------ no-allocation variant
 // A workspace in device memory the library owns: one per GPU (each device
 // holds its own copy of the array), used by mhc_post_pre_delayed_noalloc for
@@ -379,9 +391,8 @@ mhc_status pre_common(int mode, const uint16_t* x, const float* pre_in, int T, i
     // two launches: the post stage writes x_out, the delayed pre reads it
     const int C8 = C / 8;
     const long long total = (long long)T * C8;
-    hipLaunchKernelGGL(mhc_post_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), block, 0, s,
-                       reinterpret_cast<const uint4*>(pi.y), reinterpret_cast<const uint4*>(x), pi.post,
-                       pi.comb, reinterpret_cast<uint4*>(x_out), T, C8);
+    launch_post(reinterpret_cast<const uint4*>(pi.y), reinterpret_cast<const uint4*>(x), pi.post, pi.comb,
+                reinterpret_cast<uint4*>(x_out), T, C8, s);
     p.x = x_out;
     mode = kModeDelayed;
   }
@@ -545,13 +556,8 @@ mhc_status mhc_post(const uint16_t* y, const uint16_t* x, const float* post, con
   if (static_cast<const void*>(out) != static_cast<const void*>(x) && overlap(o, {x, xbytes}))
     return MHC_ERR_ALIAS;
   if (T == 0) return MHC_OK;
-  const int C8 = C / 8;
-  const long long total = (long long)T * C8;
-  const unsigned grid = (unsigned)((total + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(mhc_post_kernel, dim3(grid), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), reinterpret_cast<const uint4*>(y),
-                     reinterpret_cast<const uint4*>(x), post, comb, reinterpret_cast<uint4*>(out),
-                     T, C8);
+  launch_post(reinterpret_cast<const uint4*>(y), reinterpret_cast<const uint4*>(x), post, comb,
+              reinterpret_cast<uint4*>(out), T, C / 8, static_cast<hipStream_t>(stream));
   return launched();
 }
 

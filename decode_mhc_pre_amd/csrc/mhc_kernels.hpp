@@ -693,7 +693,10 @@ __global__ __launch_bounds__(kThreads) void mhc_collapse_kernel(PreParams p) {
 // streams (4 x 16 B), writes four streams.  Every byte is touched once, so all
 // traffic is non-temporal (streaming): measured ~14% faster than cached
 // accesses at T = 16384.  Exact in-place (out == x) is safe: a thread reads
-// all of its x before it writes.
+// all of its x before it writes.  kWaveToken (C / 8 a multiple of 64): a wave's
+// 64 threads share one token, whose 20 gate values are then loaded once per
+// wave through the scalar unit instead of by every lane.
+template <bool kWaveToken>
 __global__ __launch_bounds__(256) void mhc_post_kernel(const uint4* __restrict__ y,
                                                        const uint4* x,
                                                        const float* __restrict__ post,
@@ -701,7 +704,14 @@ __global__ __launch_bounds__(256) void mhc_post_kernel(const uint4* __restrict__
                                                        int T, int C8) {
   const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= (long long)T * C8) return;
-  const int t = (int)(idx / C8);
+  int t;
+  if constexpr (kWaveToken) {
+    // the wave's first thread is in range (it has the wave's lowest index)
+    const long long widx = (long long)blockIdx.x * kThreads + (threadIdx.x & ~(kWave - 1));
+    t = __builtin_amdgcn_readfirstlane((int)(widx / C8));
+  } else {
+    t = (int)(idx / C8);
+  }
   const int c8 = (int)(idx - (long long)t * C8);
   const size_t xb = (size_t)t * kNS * C8 + c8;
   const uint4 yq = nt_load16(y + (size_t)t * C8 + c8);
