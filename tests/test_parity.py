@@ -315,6 +315,24 @@ def post_gates(T, seed=3):
     return p, post, comb.astype(np.float32)
 
 
+@pytest.mark.parametrize("Cx,T", [(1024, 37), (1280, 37), (256, 129), (768, 51)])
+def test_post_hidden_sizes(Cx, T):
+    """mhc_post on every token at hidden sizes where a wave's 64 threads always
+    share one token (C / 8 a multiple of 64: 1024) and where waves straddle two
+    tokens (1280, 256, 768), against the oracle's exact value and bit for bit
+    against the single-precision post in the library's order."""
+    torch = torch_mod()
+    p = mi.post_inputs(T, seed=41 + Cx + T, C=Cx)
+    post = (2.0 / (1.0 + np.exp(-p["post_logit"].astype(np.float64)))).astype(np.float32)
+    comb = np.stack([oracle.sinkhorn(np.exp(m.astype(np.float64)), 20) for m in p["comb_logit"]]).astype(np.float32)
+    out = host_bits(M.mhc_post(dev_bf16(p["y"]), dev_bf16(p["x"]), dev_f32(post), dev_f32(comb)))
+    torch.cuda.synchronize()
+    say("mhc_post C=%d T=%d" % (Cx, T))
+    o = oracle.mhc_post(p["y"], p["x"], post, comb)
+    check_bf16(out, o["out_val"], o["out_mag"], what="post C=%d" % Cx)
+    assert np.array_equal(out, oracle.post32(p["y"], p["x"], post, comb))
+
+
 @pytest.mark.parametrize("T", [1, 3, 64])
 def test_post_small(T):
     torch = torch_mod()
