@@ -142,8 +142,9 @@ mhc_status mhc_debug_force_wait_timeouts(int sleeps);
  *   comb [T][n][n] float out  Sinkhorn(exp(l[8:24])), column sums 1
  *   layer_input [T][C] bf16 out  y_c = sum_i pre_i x_{i,c}, each product
  *               rounded to float and summed over i = 0..3 left to right.
- * Launches: one; with C = 5120 and T > 4096, two (the gates, then the
- * collapse with them: the collapse needs this seam's gates). */
+ * Launches: one; past the one-sweep threshold (T > 4096 at C = 4096 and 5120,
+ * T > 2048 at C = 7168), two: the gates, then the collapse with them (the
+ * collapse needs this seam's gates). */
 mhc_status mhc_pre(const uint16_t *x, int T, int n, int C, mhc_weights w,
                    const uint16_t *norm_weight, float eps, int sinkhorn_iters,
                    float *pre, float *post, float *comb, uint16_t *layer_input,
