@@ -146,11 +146,11 @@ def test_all_zero_rows(form, T):
 
 @pytest.mark.parametrize("form,T", [("delayed", 128), ("delayed", 4100), ("fused", 128), ("fused", 3100),
                                     ("own", 4100)])
-@pytest.mark.parametrize("iters", [1, 7, 33])
+@pytest.mark.parametrize("iters", [1, 7, 33, 1024])
 def test_sinkhorn_iteration_counts(form, T, iters):
-    """Iteration counts other than 20 on every kernel form (the persistent kernels
-    spread the iterations over the steps of the next tile's sweep and finish any
-    that are left when they write the gates)."""
+    """Iteration counts other than 20, up to the largest accepted (1024), on every
+    kernel form (the persistent kernels spread the iterations over the steps of
+    the next tile's sweep and finish any that are left when they write the gates)."""
     d = mi.pre_inputs(T, seed=2000 + T + iters, delayed=True, norm=True)
     d["iters"] = iters
     say("iters=%d %s T=%d" % (iters, form, T))
