@@ -169,6 +169,42 @@ def test_sinkhorn_iteration_counts(form, T, iters):
         check_fused(run_fused(d, p["y"], post_k, comb_k), d, p["y"], post_k, comb_k, what="fused iters=%d" % iters)
 
 
+@pytest.mark.parametrize("form,T", [("delayed", 128), ("delayed", 4100), ("fused", 128), ("fused", 3100),
+                                    ("own", 128), ("own", 4100), ("entry", 128)])
+@pytest.mark.parametrize("eps", [0.0, 0.5])
+def test_eps_values(form, T, eps):
+    """eps enters both root mean squares (of the 4C row for the logits, of the
+    collapsed row for the norm); at 0 and at a value comparable to the mean square
+    (0.5, inputs ~N(0,1)) a misplaced eps would move the gates and layer_input far
+    past the bar, on the split and the one-sweep forms alike."""
+    d = mi.pre_inputs(T, seed=2300 + T, delayed=True, norm=True)
+    d["eps"] = eps
+    say("eps=%g %s T=%d" % (eps, form, T))
+    if form == "delayed":
+        pre_out, post, comb, li = run_delayed(d)
+        o = oracle_delayed(d)
+        check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "delayed eps=%g" % eps)
+        check_bf16(li, o["li_val"], o["li_mag"], what="layer_input")
+    elif form == "own":
+        pre, post, comb, li = M.mhc_pre(dev_bf16(d["x"]), weights(d), dev_bf16(d["norm_weight"]), eps, d["iters"])
+        o = oracle.mhc_pre(d["x"], d["fn"], d["bias"], d["alpha"], eps, d["iters"], norm_weight=d["norm_weight"])
+        ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"], "own")
+        check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="own layer_input")
+    elif form == "entry":
+        e = mi.entry_inputs(T, seed=2400 + T)
+        x_out, pre_e, post_e, comb_e, li_e = M.mhc_broadcast_entry(dev_bf16(e["h"]), weights(e),
+                                                                  dev_bf16(e["norm_weight"]), eps, e["iters"])
+        oe = oracle.mhc_broadcast_entry(e["h"], e["fn"], e["bias"], e["alpha"], eps, e["iters"],
+                                        norm_weight=e["norm_weight"])
+        assert np.array_equal(host_bits(x_out), oe["x_out"])
+        ge = check_gates(host_f32(pre_e), host_f32(post_e), host_f32(comb_e), oe["pre"], oe["post"], oe["comb"],
+                         "entry")
+        check_bf16(host_bits(li_e), oe["li_val"], oe["li_mag"], d=2 * ge, what="entry layer_input")
+    else:
+        p, post_k, comb_k = post_gates(T, seed=2500 + T)
+        check_fused(run_fused(d, p["y"], post_k, comb_k), d, p["y"], post_k, comb_k, what="fused eps=%g" % eps)
+
+
 @pytest.mark.parametrize("T", [1, 8, 33, 128, 4160])
 def test_pre_with_norm(T):
     d = mi.pre_inputs(T, seed=200 + T, norm=True)
