@@ -82,14 +82,26 @@ __device__ __forceinline__ T& pick(T& a, T& b) {
 }
 
 // Geometry per hidden size: lines per member (kLines, at most 5: the weight
-// slice takes 24 KB per line of LDS) and members per group (kPG); kLateDelayed:
-// the delayed form reads the arrival counter one sub-step later and checks it
-// one sub-step earlier than the default schedule (measured at C = 7168, T =
-// 16384: 286.5 -> 281.3 us; no change for the fused form or at C = 4096).
+// slice takes 24 KB per line of LDS) and members per group (kPG).  kRefill: the
+// sub-step of a line at which the fused form issues the next line's loads (the
+// earliest that fits the registers and measured fastest: at C = 4096 one sub-step
+// earlier than at 5120 and 7168, T = 16384 281.6 -> 274.0 us).  kLateDelayed: the
+// delayed form reads the arrival counter one sub-step later and checks it one
+// sub-step earlier than the default schedule (C = 7168, T = 16384: 286.5 -> 281.3
+// us; no change for the fused form or at C = 4096).
 template <int kC> struct PersistGeom;
-template <> struct PersistGeom<4096> { static constexpr int kLines = 4, kPG = 16; static constexpr bool kLateDelayed = false; };
-template <> struct PersistGeom<5120> { static constexpr int kLines = 5, kPG = 16; static constexpr bool kLateDelayed = false; };
-template <> struct PersistGeom<7168> { static constexpr int kLines = 4, kPG = 28; static constexpr bool kLateDelayed = true; };
+template <> struct PersistGeom<4096> {
+  static constexpr int kLines = 4, kPG = 16, kRefill = 1;
+  static constexpr bool kLateDelayed = false;
+};
+template <> struct PersistGeom<5120> {
+  static constexpr int kLines = 5, kPG = 16, kRefill = 2;
+  static constexpr bool kLateDelayed = false;
+};
+template <> struct PersistGeom<7168> {
+  static constexpr int kLines = 4, kPG = 28, kRefill = 2;
+  static constexpr bool kLateDelayed = true;
+};
 
 constexpr int kPT = 64;                   // tokens per tile
 constexpr int kPW = 8;                    // waves per workgroup (two per SIMD)
@@ -604,9 +616,10 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
       // (fused: each output stream of the post stage at its own sub-step, from
       // opaque copies of the packed inputs -- sharing their unpacking across the
       // sub-steps would keep forty unpacked values live -- and the next line's
-      // loads at the line's third sub-step, into the buffer the previous line
-      // freed: two sub-steps more lead than at its last, 1% faster at C = 5120,
-      // T = 16384; any earlier, C = 5120 runs out of registers)
+      // loads at sub-step kRefill of the line (the second or third), into the
+      // buffer the previous line freed: at C = 5120 the third gives two sub-steps
+      // more lead than the last, 1% faster at T = 16384, and any earlier runs out
+      // of registers)
       static_for<kNS>([&](auto sc) __attribute__((always_inline)) {
 #pragma clang fp contract(off)
         constexpr int s = decltype(sc)::value;
@@ -630,7 +643,7 @@ void mhc_persist_kernel(PreParams p, int ngroups) {
           const float pw = s_g[wave][tok][s];
           const float4 c = *reinterpret_cast<const float4*>(&s_g[wave][tok][4 + 4 * s]);
           xv = post_packed8(pw, c.x, c.y, c.z, c.w, in[0], in[1], in[2], in[3], in[4]);
-          if constexpr (s == 2) refill();
+          if constexpr (s == G::kRefill) refill();
           buf_store16_nt(xv, rxo, xls[s] + u * 128, 0);
         } else {
           xv = xq[(kNS * (P * kL + u) + s) % kRing];
