@@ -9,7 +9,8 @@ synchronisation between replays: every replay must give the eager call's bits
 (the workspace's counters and records reset themselves inside each call), and
 the workspace words that calls read before writing must be back at zero.  The
 outputs are views into larger buffers whose guard bands hold a poison pattern:
-nothing may be written outside [T, ...].
+nothing may be written outside [T, ...].  The captured graphs also give each
+call's launch count: kernel nodes only, no memset or copy.
 """
 import numpy as np
 import pytest
@@ -154,3 +155,49 @@ def test_graph_replay_and_guard_bands(kind, T):
     if ws is not None:
         assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0, (kind, T)
     del g
+
+
+def _graph_node_types(graph):
+    """Types of the nodes of a captured HIP graph (hipGraphNodeType: 0 kernel, 1 memcpy,
+    2 memset, ...), read with the runtime's own graph queries."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipGraphGetNodes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]
+    hip.hipGraphNodeGetType.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
+    n = ctypes.c_size_t(0)
+    assert hip.hipGraphGetNodes(ctypes.c_void_p(graph), None, ctypes.byref(n)) == 0
+    nodes = (ctypes.c_void_p * max(1, n.value))()
+    assert hip.hipGraphGetNodes(ctypes.c_void_p(graph), nodes, ctypes.byref(n)) == 0
+    types = []
+    for i in range(n.value):
+        t = ctypes.c_int(-1)
+        assert hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(t)) == 0
+        types.append(t.value)
+    return types
+
+
+@pytest.mark.parametrize("kind,T,launches", [
+    ("delayed", 7, 1), ("delayed", 128, 1), ("delayed", 4100, 1),
+    ("own", 8, 1), ("own", 2049, 1), ("own", 4100, 2),
+    ("fused", 5, 1), ("fused", 300, 1), ("fused", 3100, 1),
+    ("entry", 16, 1), ("entry", 2100, 1), ("post", 64, 1), ("collapse", 300, 1)])
+def test_launches_per_call(kind, T, launches):
+    """What a call enqueues, read from its captured graph: kernel launches only (no
+    memset or copy node), one per call (a seam is one launch with the fused entry
+    point) except the own pre-mix past the one-sweep threshold (gates, then the
+    collapse with them)."""
+    torch = torch_mod()
+    call, gs, outs, ws = case(kind, T)
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph(keep_graph=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    types = _graph_node_types(g.raw_cuda_graph())
+    say("launches %s T=%d: node types %s" % (kind, T, types))
+    assert types == [0] * launches, types
