@@ -205,6 +205,29 @@ def test_eps_values(form, T, eps):
         check_fused(run_fused(d, p["y"], post_k, comb_k), d, p["y"], post_k, comb_k, what="fused eps=%g" % eps)
 
 
+@pytest.mark.parametrize("form", ["delayed", "fused", "own"])
+@pytest.mark.parametrize("T", [1, 2, 6, 7, 8, 64, 128, 256, 1024])
+def test_token_list(form, T):
+    """The token counts of the parity plan (the pages' test list 1/2/7/128/1024 and
+    the decode sizes around it) on every pre form with the fused norm, every token
+    against the oracle."""
+    d = mi.pre_inputs(T, seed=2600 + T, delayed=True, norm=True)
+    say("token list %s T=%d" % (form, T))
+    if form == "delayed":
+        pre_out, post, comb, li = run_delayed(d)
+        o = oracle_delayed(d)
+        check_gates(pre_out, post, comb, o["pre_out"], o["post"], o["comb"], "delayed T=%d" % T)
+        check_bf16(li, o["li_val"], o["li_mag"], what="layer_input")
+    elif form == "own":
+        pre, post, comb, li = M.mhc_pre(dev_bf16(d["x"]), weights(d), dev_bf16(d["norm_weight"]), d["eps"], d["iters"])
+        o = oracle.mhc_pre(d["x"], d["fn"], d["bias"], d["alpha"], d["eps"], d["iters"], norm_weight=d["norm_weight"])
+        ge = check_gates(host_f32(pre), host_f32(post), host_f32(comb), o["pre"], o["post"], o["comb"], "own")
+        check_bf16(host_bits(li), o["li_val"], o["li_mag"], d=2 * ge, what="own layer_input")
+    else:
+        p, post_k, comb_k = post_gates(T, seed=2700 + T)
+        check_fused(run_fused(d, p["y"], post_k, comb_k), d, p["y"], post_k, comb_k, what="fused T=%d" % T)
+
+
 @pytest.mark.parametrize("T", [1, 8, 33, 128, 4160])
 def test_pre_with_norm(T):
     d = mi.pre_inputs(T, seed=200 + T, norm=True)
