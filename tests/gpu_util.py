@@ -1,6 +1,8 @@
 """Helpers shared by the GPU tests: device transfer and the comparison bars.
 
-Bars (the benchmark spec of the seam block and the derivation in the design doc):
+Bars (the seam block's tolerances; the bf16 bound follows from one rounding to bf16
+of a single-precision value that carries at most a few single-precision roundings
+of the summed terms):
   * gates / comb: max relative error <= 1e-4 against the float64 oracle;
   * bf16 outputs: |gpu - v| <= ulp_bf16(v) + (8 * 2^-24 + d) * mag, where v is
     the oracle's exact value, mag the sum of |terms| that formed it, and d the

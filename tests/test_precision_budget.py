@@ -4,8 +4,8 @@ bf16 terms on the matrix cores, and this test measures, in double precision, wha
 the split by itself does to the gates at the hidden sizes of the pages' workloads.
 
   * one term (hi = bf16(f)): the gates miss the 1e-4 bar by two orders;
-  * two terms (hi + lo, the library's): inside the bar, with the margin recorded
-    in SPEC.md (about 4e-5 at C = 5120 and 6e-5 at C = 16384);
+  * two terms (hi + lo, the library's): inside the bar, with a margin of about
+    4e-5 at C = 5120 and 6e-5 at C = 16384;
   * three terms: float32 exactly, so no further term could help.
 """
 import numpy as np
